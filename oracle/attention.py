@@ -1,0 +1,99 @@
+"""fp64 oracle: block-causal attention of the active window over a frozen cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed, and where the pages say so:
+
+* [D2F-wiki] section "블록 단위 인과 어텐션" (block-wise causal attention): the
+  output sequence is cut into blocks of a fixed size; inside a block every
+  token attends to every other token of that block (both directions), and
+  between blocks a block attends only to blocks before it.  Because finished
+  blocks' K/V no longer change, they are kept in an ordinary KV cache.
+* [D2F-wiki] section "인터블록 병렬 디코딩" and [D2F-review] section "쉽게
+  이해하기": later blocks are predicted while earlier ones are still only
+  partly denoised.  Reading taken here: a window block attends to every
+  earlier window block, whatever its state, and to the whole cache.
+* The cache holds the prompt and the completed blocks and is visible to every
+  window token ([D2F-wiki] "블록 단위 인과 어텐션"; the window sits after the
+  cache).  Block boundaries inside the window are counted from the window's
+  first token, so the cache length need not be a multiple of the block size.
+
+Softmax scale: 1/sqrt(head_dim) unless given (the pages are silent; this is
+the usual scaled dot-product attention).  Grouped query heads: query head h
+reads KV head h // (n_heads_q // n_heads_kv).  LSE is the natural-log
+normaliser m + ln(sum exp(s - m)).
+"""
+import numpy as np
+
+from .common import as_f64
+
+
+def visible(prefix_len: int, win_rows: int, block_size: int) -> np.ndarray:
+    """Boolean [win_rows, prefix_len + win_rows]: may window row i see key j?
+
+    Keys are the cache (j < prefix_len) followed by the window.  A cached key
+    is always visible; window key j is visible to window row i when its block
+    index (j - prefix_len) // block_size is not after row i's block
+    i // block_size.
+    """
+    P, W, B = int(prefix_len), int(win_rows), int(block_size)
+    i = np.arange(W)[:, None]
+    j = np.arange(P + W)[None, :]
+    in_cache = j < P
+    key_block = (j - P) // B
+    row_block = i // B
+    return in_cache | (key_block <= row_block)
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float):
+    """Masked softmax attention of rows q [W, D] over keys k, v [N, D].
+
+    Returns (out [W, D], lse [W]) in float64.  Every row must see >= 1 key.
+    """
+    s = scale * (q @ k.T)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    out = (e @ v) / l[:, None]
+    return out, m + np.log(l)
+
+
+def block_attn(q, k_cache, v_cache, k_win, v_win, prefix_len, n_win_blocks, block_size,
+               scale=None, pairs=None):
+    """Window attention for a batch.
+
+    q        [nb][Hq][Wmax][D]     k_win, v_win [nb][Hkv][Wmax][D]
+    k_cache, v_cache [nb][Hkv][cap][D]
+    prefix_len[b], n_win_blocks[b]: host lists.
+
+    Returns (out [nb][Hq][Wmax][D], lse [nb][Hq][Wmax]) as float64; rows at or
+    past n_win_blocks[b] * block_size are NaN (they are not part of the step).
+    ``pairs`` optionally restricts the work to a list of (b, h); the other
+    heads are left NaN.
+    """
+    q = as_f64(q)
+    nb, hq, wmax, d = q.shape
+    hkv = k_cache.shape[1]
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full((nb, hq, wmax, d), np.nan)
+    lse = np.full((nb, hq, wmax), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(nb) for h in range(hq)]
+    cache_f64 = {}
+    for b, h in pairs:
+        g = h // group
+        P = int(prefix_len[b])
+        W = int(n_win_blocks[b]) * int(block_size)
+        key = (b, g)
+        if key not in cache_f64:
+            kk = np.concatenate([as_f64(k_cache[b, g, :P]), as_f64(k_win[b, g, :W])], axis=0)
+            vv = np.concatenate([as_f64(v_cache[b, g, :P]), as_f64(v_win[b, g, :W])], axis=0)
+            cache_f64 = {key: (kk, vv)}  # keep one KV head resident at a time
+        kk, vv = cache_f64[key]
+        o, l = attend(q[b, h, :W], kk, vv, visible(P, W, block_size), scale)
+        out[b, h, :W] = o
+        lse[b, h, :W] = l
+    return out, lse
