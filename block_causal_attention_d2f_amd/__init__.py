@@ -1,0 +1,13 @@
+"""block_causal_attention_d2f_amd: the hot path of one D2F denoising step on
+MI355X (gfx950), as a C-ABI HIP library (libd2f.so, see include/d2f.h) with a
+thin ctypes binding.
+
+    d2f_block_attn          block-causal attention of the active window
+    d2f_confidence_commit   max-probability confidence + commit/remask
+    d2f_kv_commit           append a completed block to the KV cache
+"""
+from ._binding import (AGGRESSIVE, COMMITTED, CONSERVATIVE, D2F_BF16, D2F_F32, EXPORTS,  # noqa: F401
+                       LIB_PATH, MASKED, AttnDesc, D2FError, d2f_block_attn,
+                       d2f_block_attn_workspace_size, d2f_confidence_commit,
+                       d2f_confidence_commit_workspace_size, d2f_kv_commit, load, make_desc,
+                       version)

@@ -1,0 +1,233 @@
+"""ctypes binding over libd2f.so (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name declared in
+include/d2f.h.  Torch tensors supply device memory and the current HIP stream;
+all arithmetic runs in the library's HIP kernels.  There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libd2f.so")
+
+D2F_OK = 0
+STATUS_NAMES = {0: "D2F_OK", 1: "D2F_ERR_INVALID_ARG", 2: "D2F_ERR_CAPACITY",
+                3: "D2F_ERR_ORDER", 4: "D2F_ERR_WORKSPACE", 5: "D2F_ERR_HIP",
+                6: "D2F_ERR_UNSUPPORTED"}
+D2F_F32, D2F_BF16 = 0, 1
+MASKED, COMMITTED = 0, 1
+CONSERVATIVE, AGGRESSIVE = 0, 1
+
+EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
+           "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
+           "d2f_status_string", "d2f_last_error", "d2f_version")
+
+
+class D2FError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
+                ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_win_blocks", ctypes.c_int32),
+                ("cache_capacity", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                              ctypes.c_size_t)
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libd2f.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(f"{p} is missing: build it with "
+                                "`python -m block_causal_attention_d2f_amd.build`")
+    lib = ctypes.CDLL(p)
+    pdesc = ctypes.POINTER(AttnDesc)
+    sig = {
+        "d2f_block_attn_workspace_size": (_i32, [pdesc, _pi32, _pi32, ctypes.POINTER(_sz)]),
+        "d2f_block_attn": (_i32, [pdesc, _vp, _vp, _vp, _vp, _vp, _pi32, _pi32, _vp, _vp, _vp,
+                                  _sz, _vp]),
+        "d2f_kv_commit": (_i32, [pdesc, _i32, _vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _pi32,
+                                 _vp, _vp]),
+        "d2f_confidence_commit_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
+        "d2f_confidence_commit": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
+                                         _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "d2f_status_string": (ctypes.c_char_p, [_i32]),
+        "d2f_last_error": (ctypes.c_char_p, []),
+        "d2f_version": (_i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != D2F_OK:
+        lib = load()
+        raise D2FError(st, lib.d2f_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _i32_array(xs: Sequence[int]):
+    return (ctypes.c_int32 * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+def make_desc(batch, n_heads_q, n_heads_kv, head_dim, block_size, max_win_blocks,
+              cache_capacity, dtype, softmax_scale=0.0) -> AttnDesc:
+    dt = {torch.float32: D2F_F32, torch.bfloat16: D2F_BF16}.get(dtype, dtype)
+    return AttnDesc(int(batch), int(n_heads_q), int(n_heads_kv), int(head_dim), int(block_size),
+                    int(max_win_blocks), int(cache_capacity), int(dt), float(softmax_scale))
+
+
+def _desc_from(q, k_cache, block_size, softmax_scale) -> AttnDesc:
+    nb, hq, wmax, d = q.shape
+    hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if wmax % block_size:
+        raise ValueError("window rows of q must be a multiple of block_size")
+    return make_desc(nb, hq, hkv, d, block_size, wmax // block_size, cap, q.dtype, softmax_scale)
+
+
+def d2f_block_attn_workspace_size(desc: AttnDesc, prefix_len, n_win_blocks) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().d2f_block_attn_workspace_size(ctypes.byref(desc), _i32_array(prefix_len),
+                                                _i32_array(n_win_blocks), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _contig(name, t, dtype=None, device=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def d2f_block_attn(q, k_cache, v_cache, k_win, v_win, prefix_len, n_win_blocks, block_size,
+                   out=None, lse=None, want_lse=True, softmax_scale=0.0, workspace=None,
+                   stream=None):
+    """Block-causal attention of the window over the frozen cache (one layer).
+
+    q [nb][Hq][Wmax][D]; k_cache, v_cache [nb][Hkv][cap][D]; k_win, v_win
+    [nb][Hkv][Wmax][D]; prefix_len, n_win_blocks: host sequences of ints.
+    Returns (out, lse); lse is None unless want_lse.
+    """
+    desc = _desc_from(q, k_cache, block_size, softmax_scale)
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_win", k_win),
+                 ("v_win", v_win)):
+        _contig(n, t, q.dtype, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    pl, nw = _i32_array(prefix_len), _i32_array(n_win_blocks)
+    need = d2f_block_attn_workspace_size(desc, prefix_len, n_win_blocks)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().d2f_block_attn(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_win), _ptr(v_win), pl, nw, _ptr(out), _ptr(lse),
+                                 _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def d2f_kv_commit(k_cache, v_cache, k_win, v_win, prefix_len: list, request: int,
+                  block_size: int, block: int = 0, prefix_len_dev=None, stream=None):
+    """Append window block `block` (must be 0, the oldest) of `request` to the
+    cache.  Accepts one layer ([nb][Hkv][cap][D]) or a stack of layers
+    ([L][nb][Hkv][cap][D]).  prefix_len (a Python list) is updated in place."""
+    layered = k_cache.dim() == 5
+    kc0 = k_cache[0] if layered else k_cache
+    kw0 = k_win[0] if layered else k_win
+    n_layers = k_cache.shape[0] if layered else 1
+    nb, hkv, cap, d = kc0.shape
+    wmax = kw0.shape[2]
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_win", k_win), ("v_win", v_win)):
+        _contig(n, t, k_cache.dtype, k_cache.device)
+    desc = make_desc(nb, hkv, hkv, d, block_size, wmax // block_size, cap, k_cache.dtype)
+    pl = _i32_array(prefix_len)
+    _check(load().d2f_kv_commit(ctypes.byref(desc), n_layers, _ptr(k_cache), _ptr(v_cache),
+                                kc0.numel(), _ptr(k_win), _ptr(v_win), kw0.numel(), int(request),
+                                int(block), pl, _ptr(prefix_len_dev), _stream(stream)))
+    prefix_len[request] = int(pl[request])
+    return prefix_len
+
+
+def d2f_confidence_commit_workspace_size(n_rows: int, vocab: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().d2f_confidence_commit_workspace_size(int(n_rows), int(vocab),
+                                                       ctypes.byref(out)))
+    return int(out.value)
+
+
+def d2f_confidence_commit(logits, mask_state, tokens, block_phase, block_size: int, tau: float,
+                          k_aggr: int = 1, mask_token_id: int = 0, conf_out=None,
+                          argmax_out=None, n_committed=None, block_complete=None,
+                          workspace=None, stream=None, want_conf=True):
+    """One commit pass.  logits [rows][V] fp32 (row stride may exceed V);
+    mask_state uint8 [rows] and tokens int32 [rows] are updated in place.
+    Returns dict(n_committed, block_complete, conf, argmax)."""
+    rows, vocab = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    dev = logits.device
+    _contig("mask_state", mask_state, torch.uint8, dev)
+    _contig("tokens", tokens, torch.int32, dev)
+    _contig("block_phase", block_phase, torch.uint8, dev)
+    n_blocks = rows // block_size if block_size > 0 else 0
+    if n_committed is None:
+        n_committed = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    if block_complete is None:
+        block_complete = torch.empty(n_blocks, dtype=torch.uint8, device=dev)
+    if want_conf and conf_out is None:
+        conf_out = torch.full((rows,), float("nan"), dtype=torch.float32, device=dev)
+    if want_conf and argmax_out is None:
+        argmax_out = torch.full((rows,), -1, dtype=torch.int32, device=dev)
+    need = d2f_confidence_commit_workspace_size(rows, vocab)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(load().d2f_confidence_commit(
+        _ptr(logits), logits.stride(0), rows, vocab, _ptr(mask_state), _ptr(tokens),
+        _ptr(block_phase), int(block_size), ctypes.c_float(tau), int(k_aggr), int(mask_token_id),
+        _ptr(conf_out), _ptr(argmax_out), _ptr(n_committed), _ptr(block_complete),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dict(n_committed=n_committed, block_complete=block_complete, conf=conf_out,
+                argmax=argmax_out)
+
+
+def version() -> int:
+    return int(load().d2f_version())
+
+
+def softmax_scale_default(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

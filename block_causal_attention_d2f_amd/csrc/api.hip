@@ -1,0 +1,362 @@
+// C entry points of libd2f: argument checks, work planning and launches.
+// The operations themselves are documented in include/d2f.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "d2f_internal.h"
+
+namespace d2f {
+namespace {
+
+thread_local std::string g_last_error;
+
+d2f_status_t fail(d2f_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+d2f_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(D2F_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Work-unit sizing: aim for this many workgroups per call (4 per CU on the
+// 256-CU part, enough to balance ragged key lengths), but never split a key
+// range into pieces shorter than kMinChunkTiles tiles.
+constexpr long long kTargetUnits = 1024;
+constexpr int kMinChunkTiles = 2;
+
+bool head_dim_supported(d2f_dtype_t dt, int d) {
+  if (dt == D2F_BF16) return d == 64 || d == 128;
+  if (dt == D2F_F32) return d == 32 || d == 64 || d == 128;
+  return false;
+}
+
+d2f_status_t check_desc(const d2f_attn_desc_t* d) {
+  if (d == nullptr) return fail(D2F_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 0) return fail(D2F_ERR_INVALID_ARG, "batch %d < 0", d->batch);
+  if (d->n_heads_q < 1 || d->n_heads_kv < 1)
+    return fail(D2F_ERR_INVALID_ARG, "head counts must be >= 1 (got %d, %d)", d->n_heads_q,
+                d->n_heads_kv);
+  if (d->n_heads_q % d->n_heads_kv != 0)
+    return fail(D2F_ERR_INVALID_ARG, "n_heads_q %d is not a multiple of n_heads_kv %d",
+                d->n_heads_q, d->n_heads_kv);
+  if (d->head_dim < 1) return fail(D2F_ERR_INVALID_ARG, "head_dim %d < 1", d->head_dim);
+  if (d->block_size < 1) return fail(D2F_ERR_INVALID_ARG, "block_size %d < 1", d->block_size);
+  if (d->max_win_blocks < 1)
+    return fail(D2F_ERR_INVALID_ARG, "max_win_blocks %d < 1", d->max_win_blocks);
+  if (d->cache_capacity < 0)
+    return fail(D2F_ERR_INVALID_ARG, "cache_capacity %lld < 0", (long long)d->cache_capacity);
+  if (d->dtype != D2F_F32 && d->dtype != D2F_BF16)
+    return fail(D2F_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
+  const long long wmax = (long long)d->max_win_blocks * d->block_size;
+  if (wmax > (1 << 20) || d->cache_capacity > (1LL << 30) ||
+      (long long)d->n_heads_q / d->n_heads_kv * wmax > (1LL << 30))
+    return fail(D2F_ERR_INVALID_ARG, "window or cache too large for 32-bit row indexing");
+  if (!std::isfinite(d->softmax_scale))
+    return fail(D2F_ERR_INVALID_ARG, "softmax_scale is not finite");
+  return D2F_OK;
+}
+
+d2f_status_t check_lengths(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin) {
+  if (d->batch == 0) return D2F_OK;
+  if (prefix == nullptr || nwin == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "prefix_len_host / n_win_blocks_host is NULL");
+  for (int b = 0; b < d->batch; ++b) {
+    if (prefix[b] < 0) return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d < 0", b, prefix[b]);
+    if (nwin[b] < 1 || nwin[b] > d->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [1, %d]", b, nwin[b],
+                  d->max_win_blocks);
+    const long long need = (long long)prefix[b] + (long long)nwin[b] * d->block_size;
+    if (need > d->cache_capacity)
+      return fail(D2F_ERR_CAPACITY, "request %d needs %lld cache slots, capacity %lld", b, need,
+                  (long long)d->cache_capacity);
+  }
+  return D2F_OK;
+}
+
+struct Launch {
+  std::vector<ReqInfo> req;
+  int n_units = 0, n_groups = 0;
+  bool any_split = false;
+};
+
+// Split the batch into launches of at most kMaxReqPerLaunch requests and size
+// every request's key splits.  Returns the workspace bytes needed.
+size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
+                      std::vector<Launch>& out) {
+  const int G = d->n_heads_q / d->n_heads_kv;
+  long long total_tiles = 0;
+  for (int b = 0; b < d->batch; ++b) {
+    const long long W = (long long)nwin[b] * d->block_size;
+    const long long qtiles = (G * W + kQTile - 1) / kQTile;
+    const long long keys = prefix[b] + W;
+    total_tiles += (long long)d->n_heads_kv * qtiles * ((keys + kKTile - 1) / kKTile);
+  }
+  const long long chunk_tiles =
+      std::max<long long>(kMinChunkTiles, (total_tiles + kTargetUnits - 1) / kTargetUnits);
+  size_t ws = 0;
+  out.clear();
+  for (int b0 = 0; b0 < d->batch; b0 += kMaxReqPerLaunch) {
+    Launch L;
+    const int b1 = std::min(d->batch, b0 + kMaxReqPerLaunch);
+    for (int b = b0; b < b1; ++b) {
+      ReqInfo r{};
+      r.b = b;
+      r.prefix = prefix[b];
+      r.win = nwin[b] * d->block_size;
+      r.qtiles = (G * r.win + kQTile - 1) / kQTile;
+      const long long tiles = (r.prefix + r.win + kKTile - 1) / kKTile;
+      r.nsplit = (int)((tiles + chunk_tiles - 1) / chunk_tiles);
+      if (r.nsplit <= 1) {
+        r.nsplit = 1;
+        r.chunk = (int)(tiles * kKTile);
+      } else {
+        r.chunk = (int)(chunk_tiles * kKTile);
+        L.any_split = true;
+      }
+      r.unit_base = L.n_units;
+      r.group_base = L.n_groups;
+      L.n_units += d->n_heads_kv * r.nsplit * r.qtiles;
+      L.n_groups += d->n_heads_kv * r.qtiles;
+      L.req.push_back(r);
+    }
+    if (L.any_split)
+      ws = std::max(ws, (size_t)L.n_units * kQTile * ((size_t)d->head_dim + 2) * sizeof(float));
+    out.push_back(std::move(L));
+  }
+  return ws;
+}
+
+size_t commit_chunks(int32_t vocab) { return (size_t)((vocab + kCommitChunk - 1) / kCommitChunk); }
+
+}  // namespace
+}  // namespace d2f
+
+using namespace d2f;
+
+extern "C" {
+
+const char* d2f_status_string(d2f_status_t s) {
+  switch (s) {
+    case D2F_OK: return "ok";
+    case D2F_ERR_INVALID_ARG: return "invalid argument";
+    case D2F_ERR_CAPACITY: return "cache capacity exceeded";
+    case D2F_ERR_ORDER: return "only the oldest window block can be committed";
+    case D2F_ERR_WORKSPACE: return "workspace missing or too small";
+    case D2F_ERR_HIP: return "HIP runtime error";
+    case D2F_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char* d2f_last_error(void) { return g_last_error.c_str(); }
+
+int32_t d2f_version(void) { return 100; }
+
+d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
+                                           const int32_t* prefix_len_host,
+                                           const int32_t* n_win_blocks_host, size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(D2F_ERR_INVALID_ARG, "bytes_out is NULL");
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if ((st = check_lengths(desc, prefix_len_host, n_win_blocks_host)) != D2F_OK) return st;
+  std::vector<Launch> plan;
+  *bytes_out = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
+  return D2F_OK;
+}
+
+d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const void* k_win, const void* v_win,
+                            const int32_t* prefix_len_host, const int32_t* n_win_blocks_host,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if ((st = check_lengths(desc, prefix_len_host, n_win_blocks_host)) != D2F_OK) return st;
+  if (!head_dim_supported(desc->dtype, desc->head_dim))
+    return fail(D2F_ERR_UNSUPPORTED, "head_dim %d is not built for dtype %d", desc->head_dim,
+                (int)desc->dtype);
+  if (desc->batch == 0) return D2F_OK;
+  bool any_prefix = false;
+  for (int b = 0; b < desc->batch; ++b) any_prefix |= prefix_len_host[b] > 0;
+  if (q == nullptr || k_win == nullptr || v_win == nullptr || out == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "q, k_win, v_win and out must not be NULL");
+  if (any_prefix && (k_cache == nullptr || v_cache == nullptr))
+    return fail(D2F_ERR_INVALID_ARG, "k_cache / v_cache is NULL but a prefix is not empty");
+  const size_t esz = desc->dtype == D2F_BF16 ? 2 : 4;
+  for (const void* p : {q, k_cache, v_cache, k_win, v_win, (const void*)out})
+    if (p != nullptr && ((uintptr_t)p % 16) != 0)
+      return fail(D2F_ERR_INVALID_ARG, "q/k/v/out buffers must be 16-byte aligned");
+  if (((size_t)desc->head_dim * esz) % 16 != 0)
+    return fail(D2F_ERR_UNSUPPORTED, "head_dim rows must be a multiple of 16 bytes");
+
+  std::vector<Launch> plan;
+  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+  if (need > 0 && ((uintptr_t)workspace % 256) != 0)
+    return fail(D2F_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  const float scale =
+      desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / std::sqrt((float)desc->head_dim);
+  hipStream_t s = (hipStream_t)stream;
+  for (const Launch& L : plan) {
+    AttnArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.kw = k_win;
+    a.vw = v_win;
+    a.out = out;
+    a.lse = lse;
+    a.ws_o = (float*)workspace;
+    a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * kQTile * desc->head_dim
+                          : nullptr;
+    a.cap = desc->cache_capacity;
+    a.hq = desc->n_heads_q;
+    a.hkv = desc->n_heads_kv;
+    a.group = desc->n_heads_q / desc->n_heads_kv;
+    a.wmax = desc->max_win_blocks * desc->block_size;
+    a.bsz = desc->block_size;
+    a.n_req = (int)L.req.size();
+    a.n_units = L.n_units;
+    a.n_groups = L.n_groups;
+    a.c2 = scale * 1.4426950408889634f;
+    for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
+    hipError_t e = desc->dtype == D2F_BF16 ? launch_attn_bf16(a, desc->head_dim, s)
+                                           : launch_attn_f32(a, desc->head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (L.any_split) {
+      e = launch_attn_merge(a, desc->head_dim, desc->dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "split merge launch");
+    }
+  }
+  return D2F_OK;
+}
+
+d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache,
+                           void* v_cache, int64_t cache_layer_stride, const void* k_win,
+                           const void* v_win, int64_t win_layer_stride, int32_t request,
+                           int32_t block, int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                           d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if (n_layers < 1) return fail(D2F_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (request < 0 || request >= desc->batch)
+    return fail(D2F_ERR_INVALID_ARG, "request %d outside [0, %d)", request, desc->batch);
+  if (block != 0)
+    return fail(D2F_ERR_ORDER, "block %d is not the oldest window block (0)", block);
+  if (prefix_len_host == nullptr) return fail(D2F_ERR_INVALID_ARG, "prefix_len_host is NULL");
+  if (k_cache == nullptr || v_cache == nullptr || k_win == nullptr || v_win == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "cache and window pointers must not be NULL");
+  const int32_t P = prefix_len_host[request];
+  if (P < 0) return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d < 0", request, P);
+  if ((long long)P + desc->block_size > desc->cache_capacity)
+    return fail(D2F_ERR_CAPACITY, "cache full: %d + %d > %lld", P, desc->block_size,
+                (long long)desc->cache_capacity);
+  const long long wmax = (long long)desc->max_win_blocks * desc->block_size;
+  const long long cache_layer = (long long)desc->batch * desc->n_heads_kv * desc->cache_capacity *
+                                desc->head_dim;
+  const long long win_layer = (long long)desc->batch * desc->n_heads_kv * wmax * desc->head_dim;
+  if (n_layers > 1 && (cache_layer_stride < cache_layer || win_layer_stride < win_layer))
+    return fail(D2F_ERR_INVALID_ARG, "layer strides smaller than one layer");
+  const int esz = desc->dtype == D2F_BF16 ? 2 : 4;
+  KvArgs a{};
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.kw = k_win;
+  a.vw = v_win;
+  a.cache_layer_stride = cache_layer_stride;
+  a.win_layer_stride = win_layer_stride;
+  a.cap = desc->cache_capacity;
+  a.n_layers = n_layers;
+  a.hkv = desc->n_heads_kv;
+  a.wmax = (int32_t)wmax;
+  a.head_dim = desc->head_dim;
+  a.bsz = desc->block_size;
+  a.esize = esz;
+  a.request = request;
+  a.prefix = P;
+  a.new_prefix = P + desc->block_size;
+  a.prefix_dev = prefix_len_dev;
+  hipError_t e = launch_kv_commit(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv commit launch");
+  prefix_len_host[request] = P + desc->block_size;
+  return D2F_OK;
+}
+
+d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
+                                                  size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(D2F_ERR_INVALID_ARG, "bytes_out is NULL");
+  if (n_rows < 0 || vocab < 1)
+    return fail(D2F_ERR_INVALID_ARG, "n_rows %d / vocab %d out of range", n_rows, vocab);
+  *bytes_out = (size_t)n_rows * commit_chunks(vocab) * sizeof(float4);
+  return D2F_OK;
+}
+
+d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_rows,
+                                   int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                   const uint8_t* block_phase, int32_t block_size, float tau,
+                                   int32_t k_aggr, int32_t mask_token_id, float* conf_out,
+                                   int32_t* argmax_out, int32_t* n_committed,
+                                   uint8_t* block_complete, void* workspace,
+                                   size_t workspace_bytes, d2f_stream_t stream) {
+  if (n_rows < 0 || vocab < 1 || ld < vocab)
+    return fail(D2F_ERR_INVALID_ARG, "n_rows %d, vocab %d, ld %lld out of range", n_rows, vocab,
+                (long long)ld);
+  if (block_size < 1 || n_rows % block_size != 0)
+    return fail(D2F_ERR_INVALID_ARG, "n_rows %d is not a multiple of block_size %d", n_rows,
+                block_size);
+  if (block_size > kMaxCommitBlock)
+    return fail(D2F_ERR_UNSUPPORTED, "block_size %d > %d", block_size, kMaxCommitBlock);
+  if (k_aggr < 0) return fail(D2F_ERR_INVALID_ARG, "k_aggr %d < 0", k_aggr);
+  if (std::isnan(tau)) return fail(D2F_ERR_INVALID_ARG, "tau is NaN");
+  if (n_rows == 0) return D2F_OK;
+  if (logits == nullptr || mask_state == nullptr || tokens == nullptr || block_phase == nullptr ||
+      n_committed == nullptr || block_complete == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "a required pointer is NULL");
+  const size_t n_chunks = commit_chunks(vocab);
+  const size_t need = (size_t)n_rows * n_chunks * sizeof(float4);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+  if (((uintptr_t)workspace % 16) != 0)
+    return fail(D2F_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if ((unsigned long long)n_rows * n_chunks > 0x7fffffffULL)
+    return fail(D2F_ERR_UNSUPPORTED, "too many rows x chunks for one launch");
+  CommitArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.n_rows = n_rows;
+  a.vocab = vocab;
+  a.n_chunks = (int32_t)n_chunks;
+  a.chunk = kCommitChunk;
+  a.block_size = block_size;
+  a.k_aggr = k_aggr;
+  a.mask_token_id = mask_token_id;
+  a.tau = tau;
+  a.mask_state = mask_state;
+  a.tokens = tokens;
+  a.block_phase = block_phase;
+  a.conf_out = conf_out;
+  a.argmax_out = argmax_out;
+  a.n_committed = n_committed;
+  a.block_complete = block_complete;
+  a.partial = (float4*)workspace;
+  const bool vec4 = ((uintptr_t)logits % 16) == 0 && (ld % 4) == 0;
+  hipError_t e = launch_confidence_commit(a, vec4, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "confidence commit launch");
+  return D2F_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal declarations shared by the libd2f translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/d2f.h"
+
+namespace d2f {
+
+// Attention work decomposition.  A work unit is one workgroup: one request,
+// one KV head, one tile of kQTile query rows and one contiguous range of keys
+// (a "split").  Query rows of a KV head are the (window position, head in the
+// group) pairs, flattened position-major: row r <-> i = r / group,
+// head = kv_head * group + r % group, so one tile covers a contiguous run of
+// window positions, hence of D2F blocks.
+constexpr int kQTile = 64;   // query rows per workgroup
+constexpr int kKTile = 64;   // keys per K/V tile
+constexpr int kMaxReqPerLaunch = 64;
+constexpr int kAttnThreads = 256;
+
+struct ReqInfo {
+  int32_t b;          // batch index of the request
+  int32_t prefix;     // P: cached tokens
+  int32_t win;        // W: window tokens (n_win_blocks * block_size)
+  int32_t qtiles;     // ceil(group * W / kQTile)
+  int32_t nsplit;     // key-range splits (1 = the unit writes final outputs)
+  int32_t chunk;      // keys per split, a multiple of kKTile
+  int32_t unit_base;  // first work unit of this request within the launch
+  int32_t group_base; // first (kv_head, qtile) merge group within the launch
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kw;
+  const void* vw;
+  void* out;
+  float* lse;
+  float* ws_o;   // [unit][kQTile][D] unnormalised partial outputs
+  float* ws_ml;  // [unit][kQTile][2] running max (log2 units) and sum
+  int64_t cap;   // cache slots per (request, KV head)
+  int32_t hq, hkv, group, wmax, bsz;
+  int32_t n_req, n_units, n_groups;
+  float c2;      // softmax scale * log2(e)
+  ReqInfo req[kMaxReqPerLaunch];
+};
+
+// Locate the request of a work unit (unit_base is increasing).
+__device__ __forceinline__ int find_req(const AttnArgs& a, int u) {
+  int lo = 0, hi = a.n_req - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a.req[mid].unit_base <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int find_req_group(const AttnArgs& a, int g) {
+  int lo = 0, hi = a.n_req - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a.req[mid].group_base <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup x runs on XCD
+// x % 8).  Renumber so that each XCD receives a contiguous run of logical
+// units: neighbouring units (the query tiles of one KV range) then share that
+// XCD's L2.
+__device__ __forceinline__ int xcd_remap(int x, int n) {
+  const int q = n >> 3, r = n & 7, k = x & 7, j = x >> 3;
+  return (k < r) ? k * (q + 1) + j : r * (q + 1) + (k - r) * q + j;
+}
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, d2f_dtype_t dt, hipStream_t s);
+
+struct CommitArgs {
+  const float* logits;
+  int64_t ld;
+  int32_t n_rows, vocab, n_chunks, chunk, block_size, k_aggr, mask_token_id;
+  float tau;
+  uint8_t* mask_state;
+  int32_t* tokens;
+  const uint8_t* block_phase;
+  float* conf_out;
+  int32_t* argmax_out;
+  int32_t* n_committed;
+  uint8_t* block_complete;
+  float4* partial;  // [row][chunk] = {max, sum, argmax bits, unused}
+};
+constexpr int kCommitThreads = 256;
+constexpr int kCommitChunk = 8192;     // logits per workgroup (32 KiB)
+constexpr int kMaxCommitBlock = 1024;  // rows per D2F block handled by one workgroup
+hipError_t launch_confidence_commit(const CommitArgs& a, bool vec4, hipStream_t s);
+
+struct KvArgs {
+  void* kc;
+  void* vc;
+  const void* kw;
+  const void* vw;
+  int64_t cache_layer_stride, win_layer_stride;  // elements
+  int64_t cap;
+  int32_t n_layers, hkv, wmax, head_dim, bsz, esize, request, prefix, new_prefix;
+  int32_t* prefix_dev;
+};
+hipError_t launch_kv_commit(const KvArgs& a, hipStream_t s);
+
+}  // namespace d2f

@@ -1,0 +1,217 @@
+/*
+ * d2f.h -- C interface of libd2f, the hot path of one D2F (Discrete Diffusion
+ * Forcing) denoising step on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *  [D2F-wiki]    "D2F: 확산 언어 모델이 KV 캐시를 얻고 자기회귀 모델보다 2.5배
+ *                빨라지는 방법 (arXiv:2508.09192)", llm-wiki.hwlabs.dev
+ *  [D2F-review]  "D2F 논문 리뷰: 확산 LLM이 자기회귀 모델보다 빠른 추론을
+ *                처음으로 달성한 방식", allinfo.ai.kr
+ *  [dLLM-survey] "확산 언어 모델(Diffusion LLM)이란 무엇인가", discuss.pytorch.kr
+ *
+ * One step of D2F decoding runs, per layer, attention of the active window's
+ * tokens over the frozen KV cache plus the window itself (d2f_block_attn),
+ * then one pass over the vocabulary logits of the window positions that
+ * decides which positions to commit (d2f_confidence_commit), and, when the
+ * oldest window block is complete, moves that block's K/V into the cache
+ * (d2f_kv_commit).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named *_host are host memory read synchronously during the
+ *    call.  All other buffers are device memory owned by the caller; the
+ *    library allocates nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and is complete
+ *    once the stream is synchronised.  Calls on different streams are
+ *    independent; calls that share buffers must be ordered by the caller.
+ *  - Every entry point returns a d2f_status_t.  On any status other than
+ *    D2F_OK and D2F_ERR_HIP nothing was enqueued.  D2F_ERR_HIP reports a
+ *    failed launch; d2f_last_error() then holds a message (per thread).
+ *  - Results are deterministic for fixed inputs: no floating-point atomics.
+ *  - Device buffers must be naturally aligned for their element type; the
+ *    fast paths additionally use 16-byte vector accesses when rows allow it.
+ */
+#ifndef D2F_H
+#define D2F_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (a pointer to the runtime's opaque stream). */
+struct ihipStream_t;
+typedef struct ihipStream_t* d2f_stream_t;
+
+typedef enum {
+  D2F_OK = 0,
+  D2F_ERR_INVALID_ARG = 1, /* a size, pointer or enum is out of range          */
+  D2F_ERR_CAPACITY = 2,    /* the cache cannot hold the requested tokens       */
+  D2F_ERR_ORDER = 3,       /* kv_commit of a block other than the oldest one   */
+  D2F_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required       */
+  D2F_ERR_HIP = 5,         /* a HIP launch or runtime call failed              */
+  D2F_ERR_UNSUPPORTED = 6  /* valid, but not a shape this build handles        */
+} d2f_status_t;
+
+typedef enum { D2F_F32 = 0, D2F_BF16 = 1 } d2f_dtype_t;
+
+/* mask_state values (uint8 per window position) */
+enum { D2F_MASKED = 0, D2F_COMMITTED = 1 };
+/* block_phase values (uint8 per window block) */
+enum { D2F_CONSERVATIVE = 0, D2F_AGGRESSIVE = 1 };
+
+/* Geometry of the attention of one layer.
+ *  batch           requests in the call (>= 0)
+ *  n_heads_q       query heads; n_heads_kv KV heads; n_heads_q % n_heads_kv == 0
+ *                  and query head h reads KV head h / (n_heads_q / n_heads_kv)
+ *  head_dim        D: 128 for bf16 (the MFMA path); 32, 64 or 128 for f32
+ *  block_size      B >= 1, tokens per D2F block
+ *  max_win_blocks  window capacity in blocks; Wmax = max_win_blocks * B
+ *  cache_capacity  token slots per (request, KV head) in the cache arrays
+ *  dtype           element type of q, k_*, v_* and out
+ *  softmax_scale   scores are scale * <q, k>; <= 0 selects 1/sqrt(head_dim)
+ */
+typedef struct {
+  int32_t batch;
+  int32_t n_heads_q;
+  int32_t n_heads_kv;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_win_blocks;
+  int64_t cache_capacity;
+  d2f_dtype_t dtype;
+  float softmax_scale;
+} d2f_attn_desc_t;
+
+/* Bytes of device workspace d2f_block_attn needs for these lengths (0 when
+ * no key range is split).  Same argument rules as d2f_block_attn. */
+d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
+                                           const int32_t* prefix_len_host,
+                                           const int32_t* n_win_blocks_host,
+                                           size_t* bytes_out);
+
+/* Block-causal attention of the active window over the frozen cache.
+ *
+ * [D2F-wiki] section "블록 단위 인과 어텐션": the sequence is split into
+ * blocks of B tokens; tokens of one block attend to each other in both
+ * directions, a block attends only to the blocks before it, and completed
+ * blocks' K/V sit unchanged in a KV cache.  [D2F-wiki] "인터블록 병렬
+ * 디코딩" and [D2F-review] "쉽게 이해하기": later blocks are decoded while
+ * earlier ones are still partly masked, so a window block also attends to
+ * every earlier window block.
+ *
+ * For request b (P = prefix_len_host[b], W = n_win_blocks_host[b] * B), query
+ * head h, KV head g = h / (n_heads_q / n_heads_kv) and window row i < W, the
+ * keys are the P cached tokens followed by the W window tokens; window key j
+ * is visible iff j / B <= i / B (blocks counted from the window start), and
+ * every cached key is visible.  out = softmax(scale * q K^T) V over the
+ * visible keys; lse = the natural-log normaliser of the same softmax.
+ *
+ * Layouts (row-major, dtype elements):
+ *   q, out          [batch][n_heads_q][Wmax][head_dim]
+ *   k_cache,v_cache [batch][n_heads_kv][cache_capacity][head_dim]
+ *   k_win, v_win    [batch][n_heads_kv][Wmax][head_dim]
+ *   lse             [batch][n_heads_q][Wmax] float, or NULL
+ *   prefix_len_host [batch], 0 <= P and P + W <= cache_capacity
+ *   n_win_blocks_host [batch], 1 <= n <= max_win_blocks
+ * Rows i >= W of out and lse are left untouched; cache slots >= P and window
+ * rows >= W are never read.  workspace: >= d2f_block_attn_workspace_size
+ * bytes of device memory, 256-byte aligned (may be NULL when that is 0).
+ * Errors: D2F_ERR_INVALID_ARG (bad sizes, null required pointers, group
+ * mismatch), D2F_ERR_CAPACITY (P + W > cache_capacity), D2F_ERR_WORKSPACE,
+ * D2F_ERR_UNSUPPORTED (head_dim/dtype pair not built), D2F_ERR_HIP.
+ */
+d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const void* k_cache,
+                            const void* v_cache, const void* k_win, const void* v_win,
+                            const int32_t* prefix_len_host, const int32_t* n_win_blocks_host,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            d2f_stream_t stream);
+
+/* Append the oldest window block of one request to the KV cache.
+ *
+ * [D2F-wiki] section "블록 단위 인과 어텐션": a completed block's K/V do not
+ * change any more, so an ordinary KV cache holds them exactly; section
+ * "KV 캐시 관리 방식": the completion of a block is the signal to make its
+ * cache entries permanent.
+ *
+ * For every layer l < n_layers and KV head g: rows [0, B) of window block 0
+ *   k_win + l*win_layer_stride  [batch][n_heads_kv][Wmax][head_dim]
+ * are copied bit for bit to cache slots [P, P + B) of
+ *   k_cache + l*cache_layer_stride  [batch][n_heads_kv][cache_capacity][head_dim]
+ * (likewise V), for request `request`, where P = prefix_len_host[request].
+ * Strides are in elements.  Then prefix_len_host[request] += B on the host,
+ * and, when prefix_len_dev is not NULL, prefix_len_dev[request] is set to the
+ * new value on `stream`.  The window itself is not modified: dropping the
+ * block from the window is the caller's bookkeeping.  The caller guarantees
+ * the block is complete (every position committed) and that its K/V were
+ * computed from the committed tokens.
+ * Errors: D2F_ERR_ORDER (block != 0: only the oldest window block may join
+ * the cache, which keeps the cache one contiguous prefix), D2F_ERR_CAPACITY
+ * (P + B > cache_capacity), D2F_ERR_INVALID_ARG, D2F_ERR_HIP.
+ */
+d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache,
+                           void* v_cache, int64_t cache_layer_stride, const void* k_win,
+                           const void* v_win, int64_t win_layer_stride, int32_t request,
+                           int32_t block, int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                           d2f_stream_t stream);
+
+/* Bytes of device workspace d2f_confidence_commit needs. */
+d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
+                                                  size_t* bytes_out);
+
+/* Confidence, argmax and the commit/remask decision over the window.
+ *
+ * [D2F-review] section "쉽게 이해하기": a block newly added to the window is
+ * conservative and commits only positions whose confidence exceeds the
+ * threshold; a block whose predecessor has progressed far enough is
+ * aggressive and commits the relatively most confident positions even if
+ * they are not very confident; positions not committed are masked again.
+ * [dLLM-survey] sections "양방향 어텐션과 사라진 KV 캐시" (low-confidence
+ * remasking) and "답을 미리 안다: 조기 확정 디코딩(Prophet)" (the maximum
+ * softmax probability as the confidence).
+ *
+ * Row p of `logits` (float, row stride ld >= vocab elements) holds window
+ * position p; rows of all requests are concatenated block by block, so
+ * n_rows = n_blocks * block_size.  For each row with mask_state == MASKED:
+ *   conf = max_j softmax(logits[p])_j, argmax = the smallest j reaching the max.
+ * Rows already COMMITTED are not read and not changed.  For block k
+ * (rows [k*B, (k+1)*B)), with the float threshold tau:
+ *   CONSERVATIVE: commit p iff conf_p > tau;
+ *   AGGRESSIVE:   commit p iff conf_p > tau, or p is among the k_aggr most
+ *                 confident MASKED rows of the block (ties: lower p first).
+ * A committed row gets mask_state = COMMITTED and tokens = argmax; a MASKED
+ * row that is not committed gets tokens = mask_token_id (remask).
+ * n_committed[k] = rows committed by this call; block_complete[k] = 1 iff
+ * every row of block k is COMMITTED afterwards.  conf_out / argmax_out
+ * (optional, NULL allowed) receive conf and argmax of the rows that were
+ * MASKED on entry; other rows are untouched.
+ * Buffers: mask_state uint8 [n_rows] and tokens int32 [n_rows] in/out;
+ * block_phase uint8 [n_blocks]; n_committed int32 [n_blocks] and
+ * block_complete uint8 [n_blocks] out.  Logits must be finite.
+ * Errors: D2F_ERR_INVALID_ARG (n_rows % block_size != 0, vocab < 1,
+ * ld < vocab, null required pointers, k_aggr < 0), D2F_ERR_WORKSPACE,
+ * D2F_ERR_HIP.
+ */
+d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_rows,
+                                   int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                   const uint8_t* block_phase, int32_t block_size, float tau,
+                                   int32_t k_aggr, int32_t mask_token_id, float* conf_out,
+                                   int32_t* argmax_out, int32_t* n_committed,
+                                   uint8_t* block_complete, void* workspace,
+                                   size_t workspace_bytes, d2f_stream_t stream);
+
+/* Static text for a status code. */
+const char* d2f_status_string(d2f_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* d2f_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t d2f_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* D2F_H */

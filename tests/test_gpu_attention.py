@@ -1,0 +1,110 @@
+"""GPU parity of d2f_block_attn (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import compare_attn, oracle_attn, poisoned_inputs, run_attn, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(shape, seed=0, pairs=None, label="", layer=0):
+    say(f"--- attention case {label}: {shape}")
+    x = poisoned_inputs(shape, seed=seed, layer=layer)
+    out, lse = run_attn(shape, x, out_fill=7.0)
+    ref_o, ref_l = oracle_attn(shape, x, pairs=pairs)
+    stats = compare_attn(shape, out, lse, ref_o, ref_l, pairs=pairs, label=label)
+    # Rows past each request's window are left untouched.
+    o = out.float().cpu().numpy()
+    for b in range(shape.batch):
+        assert (o[b, :, shape.win_rows(b):] == 7.0).all()
+    return x, out, lse, stats
+
+
+def test_cfg1_tiny_fp32():
+    c = W.config("cfg1")
+    _check(c["shape"], label="cfg1")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [
+    # (nb, Hq, Hkv, D, B, prefix, nwin)
+    (1, 2, 2, 64, 16, [0], [1]),            # no cache, single block
+    (1, 2, 2, 64, 16, [0], [4]),            # no cache, 4 blocks
+    (1, 4, 4, 64, 1, [37], [9]),            # B = 1: causal attention
+    (1, 2, 2, 128, 5, [77], [3]),           # B does not divide the tile; ragged prefix
+    (2, 8, 2, 64, 16, [130, 5], [2, 3]),    # GQA group 4, ragged batch
+    (3, 4, 1, 128, 8, [1000, 64, 999], [4, 1, 2]),   # many key splits, GQA 4
+    (1, 2, 2, 128, 64, [129], [3]),         # large B: window 192 rows > one query tile
+    (1, 6, 2, 64, 48, [10], [2]),           # group 3, block straddles query tiles
+])
+def test_edge_shapes(dtype, case):
+    nb, hq, hkv, d, b, prefix, nwin = case
+    shape = W.make_shape(nb, hq, hkv, d, b, prefix, nwin, dtype=dtype, extra_capacity=3)
+    _check(shape, seed=sum(prefix) + b, label=f"edge-{dtype}")
+
+
+def test_fp32_head_dim_32_long_prefix():
+    shape = W.make_shape(2, 2, 2, 32, 16, [700, 33], [3, 2], dtype="f32")
+    _check(shape, label="f32-d32-split")
+
+
+def test_explicit_softmax_scale():
+    shape = W.make_shape(1, 2, 2, 64, 16, [100], [2], dtype="f32")
+    x = poisoned_inputs(shape, seed=3)
+    out, lse = run_attn(shape, x, softmax_scale=0.3)
+    ro, rl = oracle_attn(shape, x, scale=0.3)
+    compare_attn(shape, out, lse, ro, rl, label="scale0.3")
+
+
+def test_cfg2_llada_single_step():
+    c = W.config("cfg2")
+    _check(c["shape"], label="cfg2")
+
+
+def test_cfg3_ragged_batch_layers():
+    c = W.config("cfg3")
+    sh = c["shape"]
+    _check(sh, label="cfg3-L0", layer=0)
+    rng = np.random.default_rng(3)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, sh.batch, 24),
+                                              rng.integers(0, sh.n_heads_q, 24))]
+    _check(sh, pairs=pairs, label="cfg3-L31-sampled", layer=31)
+
+
+@pytest.mark.parametrize("bsz", [16, 32, 64])
+def test_cfg4_dream_gqa(bsz):
+    c = W.config("cfg4", block_size=bsz)
+    sh = c["shape"]
+    pairs = [(0, h) for h in range(sh.n_heads_q)] + [(5, h) for h in (0, 6, 7, 13, 20, 27)]
+    _check(sh, pairs=pairs, label=f"cfg4-B{bsz}")
+
+
+def test_cfg5_long_context():
+    c = W.config("cfg5")
+    sh = c["shape"]
+    pairs = [(0, h) for h in (0, 9, 17, 31)]
+    _check(sh, pairs=pairs, label="cfg5")
+
+
+def test_deterministic_and_later_blocks_do_not_leak():
+    shape = W.make_shape(2, 4, 2, 128, 16, [300, 1500], [4, 3], dtype="bf16")
+    x = poisoned_inputs(shape, seed=11)
+    o1, l1 = run_attn(shape, x, out_fill=0.0)
+    o2, l2 = run_attn(shape, x, out_fill=0.0)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # Re-draw q/K/V of window blocks >= 2: rows of blocks 0..1 must not change.
+    y = {k: v.clone() for k, v in x.items()}
+    lo = 2 * shape.block_size
+    g = torch.Generator(device="cuda").manual_seed(99)
+    for n in ("q", "k_win", "v_win"):
+        for b in range(shape.batch):
+            hi = shape.win_rows(b)
+            r = torch.randn(y[n][b, :, lo:hi].shape, generator=g, device="cuda")
+            y[n][b, :, lo:hi] = r.to(y[n].dtype)
+    o3, l3 = run_attn(shape, y, out_fill=0.0)
+    assert torch.equal(o3[:, :, :lo], o1[:, :, :lo])
+    assert torch.equal(l3[:, :, :lo], l1[:, :, :lo])
+    assert not torch.equal(o3[0, :, lo:64], o1[0, :, lo:64])
+    say("[attn determinism/causality] ok")
