@@ -1,0 +1,390 @@
+#!/usr/bin/env python3
+"""Throughput of one D2F denoising step on one MI355X.
+
+A step is the whole hot path over one synthetic batch, through the C ABI:
+block-causal window attention for every layer of the workload
+(d2f_block_attn), the confidence/commit pass over the window's vocabulary
+logits (d2f_confidence_commit), and the append of a completed block to every
+layer's KV cache (d2f_kv_commit).  Inputs are resident in HBM before timing.
+Input sets rotate so that the timed steps read HBM rather than the 256 MB
+Infinity Cache, and every step gets its own pristine mask state.
+
+    python bench.py [--steps K] [--warmup W] [--config cfg2]
+
+prints one JSON line.  `value` is the step's compulsory HBM bytes (K/V once
+per KV head, Q, O, LSE, the masked rows' logits, the KV append) divided by
+the measured step time.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "D2F step block-attn TFLOP/s + KV/logit GB/s (frac of peak), LLaDA-8B shape"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3     # MI355X fp32 vector
+ROTATE_BYTES = 640 << 20     # > 2x the 256 MB Infinity Cache
+
+
+def attn_flops(sh):
+    """Visible (query, key) pairs x 4 * head_dim (QK^T and PV)."""
+    tot = 0.0
+    for b in range(sh.batch):
+        for k in range(sh.n_win_blocks[b]):
+            tot += sh.block_size * (sh.prefix_len[b] + (k + 1) * sh.block_size)
+    return tot * sh.n_heads_q * 4.0 * sh.head_dim
+
+
+def attn_bytes(sh):
+    """K and V once per KV head over P + W keys, Q in, O and LSE out."""
+    s = 4 if sh.dtype == "f32" else 2
+    tot = 0.0
+    for b in range(sh.batch):
+        w = sh.win_rows(b)
+        tot += sh.n_heads_kv * (sh.prefix_len[b] + w) * sh.head_dim * 2 * s
+        tot += 2 * sh.n_heads_q * w * sh.head_dim * s + sh.n_heads_q * w * 4
+    return tot
+
+
+def attn_kv_bytes(sh):
+    s = 4 if sh.dtype == "f32" else 2
+    return float(sum(sh.n_heads_kv * (sh.prefix_len[b] + sh.win_rows(b)) * sh.head_dim * 2 * s
+                     for b in range(sh.batch)))
+
+
+def commit_bytes(n_masked, rows, vocab):
+    """Masked rows' logits once, plus per-row state (mask r/w, token, conf, argmax)."""
+    return float(n_masked) * vocab * 4 + rows * (1 + 1 + 4 + 4 + 4)
+
+
+def kv_commit_bytes(sh, layers):
+    s = 4 if sh.dtype == "f32" else 2
+    return 2.0 * 2 * sh.block_size * sh.n_heads_kv * sh.head_dim * s * layers  # K+V, read+write
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
+    ap.add_argument("--block-size", type=int, default=None, help="cfg4 block size (16/32/64)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Workload:
+    """Rotating input sets of one configuration, resident on the GPU."""
+
+    def __init__(self, name, block_size, n_masks):
+        import torch
+        import workloads as W
+        self.cfg = W.config(name, block_size=block_size)
+        self.sh = sh = self.cfg["shape"]
+        self.layers = self.cfg["layers"]
+        self.tau = self.cfg["taus"][0]
+        self.k_aggr = self.cfg["k_aggr"]
+        dev = "cuda"
+        self.rows = W.total_rows(sh)
+        es = 4 if sh.dtype == "f32" else 2
+        read_per_step = (self.layers * attn_bytes(sh) + self.rows * self.cfg["vocab"] * 4)
+        # Enough input sets that the bytes streamed between two reads of the
+        # same set exceed the rotation budget (the cache cannot serve them).
+        self.n_sets = 1 + math.ceil(ROTATE_BYTES / read_per_step)
+        self.set_bytes = (self.layers * es * sh.head_dim *
+                          (sh.batch * sh.n_heads_q * sh.w_max + 2 * sh.batch * sh.n_heads_kv *
+                           (sh.cache_capacity + sh.w_max)) + self.rows * self.cfg["vocab"] * 4)
+        self.sets = []
+        for r in range(self.n_sets):
+            xs = [W.attn_inputs(sh, layer=l, device=dev, seed=r * 7919) for l in range(self.layers)]
+            st = {n: torch.stack([x[n] for x in xs]) for n in xs[0]}
+            ci = W.config_commit_inputs(self.cfg, device=dev, seed=r * 7919)
+            st["logits"] = ci.logits
+            self.sets.append(st)
+            del xs
+        self.phases = ci.block_phase
+        self.mask_token_id = ci.mask_token_id
+        self.n_masked = int((ci.mask_state == W.MASKED).sum())
+        self.mask0, self.tok0 = ci.mask_state.clone(), ci.tokens.clone()
+        self.masks = ci.mask_state.unsqueeze(0).repeat(n_masks, 1).contiguous()
+        self.tokens = ci.tokens.unsqueeze(0).repeat(n_masks, 1).contiguous()
+        # Outputs and workspaces, allocated once.
+        import block_causal_attention_d2f_amd as d2f
+        q0 = self.sets[0]["q"][0]
+        self.out = torch.empty((self.layers,) + tuple(q0.shape), dtype=q0.dtype, device=dev)
+        self.lse = torch.empty((self.layers,) + tuple(q0.shape[:3]), dtype=torch.float32,
+                               device=dev)
+        desc = d2f.make_desc(sh.batch, sh.n_heads_q, sh.n_heads_kv, sh.head_dim, sh.block_size,
+                             sh.max_win_blocks, sh.cache_capacity, q0.dtype)
+        need = d2f.d2f_block_attn_workspace_size(desc, sh.prefix_len, sh.n_win_blocks)
+        self.ws_attn = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        need = d2f.d2f_confidence_commit_workspace_size(self.rows, self.cfg["vocab"])
+        self.ws_commit = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        nb = self.rows // sh.block_size
+        self.n_committed = torch.empty(nb, dtype=torch.int32, device=dev)
+        self.block_complete = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.conf = torch.empty(self.rows, dtype=torch.float32, device=dev)
+        self.argmax = torch.empty(self.rows, dtype=torch.int32, device=dev)
+        self.prefix_dev = torch.tensor(sh.prefix_len, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    # --- the three calls ---------------------------------------------------
+    def attn(self, r, l):
+        import block_causal_attention_d2f_amd as d2f
+        s, sh = self.sets[r], self.sh
+        d2f.d2f_block_attn(s["q"][l], s["k_cache"][l], s["v_cache"][l], s["k_win"][l],
+                           s["v_win"][l], sh.prefix_len, sh.n_win_blocks, sh.block_size,
+                           out=self.out[l], lse=self.lse[l], workspace=self.ws_attn)
+
+    def commit(self, r, m):
+        import block_causal_attention_d2f_amd as d2f
+        d2f.d2f_confidence_commit(self.sets[r]["logits"], self.masks[m], self.tokens[m],
+                                  self.phases, self.sh.block_size, self.tau, self.k_aggr,
+                                  self.mask_token_id, conf_out=self.conf, argmax_out=self.argmax,
+                                  n_committed=self.n_committed,
+                                  block_complete=self.block_complete, workspace=self.ws_commit)
+
+    def kv(self, r):
+        import block_causal_attention_d2f_amd as d2f
+        s = self.sets[r]
+        prefix = list(self.sh.prefix_len)  # the workload stays fixed from step to step
+        d2f.d2f_kv_commit(s["k_cache"], s["v_cache"], s["k_win"], s["v_win"], prefix, 0,
+                          self.sh.block_size, prefix_len_dev=self.prefix_dev)
+
+    def step(self, i):
+        r = i % self.n_sets
+        for l in range(self.layers):
+            self.attn(r, l)
+        self.commit(r, i)
+        self.kv(r)
+
+    def step_bytes(self):
+        return (self.layers * attn_bytes(self.sh) +
+                commit_bytes(self.n_masked, self.rows, self.cfg["vocab"]) +
+                kv_commit_bytes(self.sh, self.layers))
+
+
+def capture(fn, use_graph):
+    """A callable that replays fn (captured into a HIP graph) or runs it."""
+    import torch
+    if not use_graph:
+        return fn
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g.replay
+
+
+def time_region(run):
+    import torch
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3
+
+
+def per_call_times(wl, reps, use_graph):
+    """Average duration of each call, from HIP events around a graph of
+    `reps` back-to-back launches on the current stream (rotating inputs)."""
+    n_sets = wl.n_sets
+    base = wl.masks.shape[0] - reps  # spare pristine masks reserved for this
+
+    def attn_run():
+        for i in range(reps):
+            wl.attn(i % n_sets, 0)
+
+    def commit_run():
+        for i in range(reps):
+            wl.commit(i % n_sets, base + i)
+
+    def kv_run():
+        for i in range(reps):
+            wl.kv(i % n_sets)
+
+    out = {}
+    for name, fn in (("d2f_block_attn", attn_run), ("d2f_confidence_commit", commit_run),
+                     ("d2f_kv_commit", kv_run)):
+        run = capture(fn, use_graph)
+        if name == "d2f_confidence_commit":
+            wl.masks[base:] = wl.mask0
+            wl.tokens[base:] = wl.tok0
+        run()  # warm
+        if name == "d2f_confidence_commit":
+            wl.masks[base:] = wl.mask0
+            wl.tokens[base:] = wl.tok0
+        ms, _ = time_region(run)
+        out[name] = ms / reps
+    return out
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle on a bounded sample of the same workload, timed on the
+    host cores.  The sample is one layer's attention for a subset of query
+    heads plus the commit pass on a subset of blocks; its compulsory bytes
+    are scaled the same way as the GPU step's."""
+    import numpy as np
+    import torch
+    from oracle import attention as OA
+    from oracle import commit as OC
+    sh = wl.sh
+    s = wl.sets[0]
+    # Copy the sample to host memory first so that only the oracle is timed.
+    heads = list(range(min(sh.n_heads_q, 8)))
+    pairs = [(b, h) for b in range(sh.batch) for h in heads]
+    host = {n: s[n][0].cpu() for n in ("q", "k_cache", "v_cache", "k_win", "v_win")}
+    nb_blocks = min(wl.rows // sh.block_size, 4)
+    rows = nb_blocks * sh.block_size
+    logits = s["logits"][:rows].cpu()
+    masks, toks = wl.mask0[:rows].cpu(), wl.tok0[:rows].cpu()
+    phases = wl.phases[:nb_blocks].cpu()
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    # bytes the sample covers, counted like the GPU step
+    frac_heads = len(heads) / sh.n_heads_q
+    bytes_attn = attn_bytes(sh) * frac_heads
+    bytes_commit = commit_bytes(int((masks == 0).sum()), rows, wl.cfg["vocab"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        OA.block_attn(host["q"], host["k_cache"], host["v_cache"], host["k_win"], host["v_win"],
+                      sh.prefix_len, sh.n_win_blocks, sh.block_size, pairs=pairs)
+        OC.confidence_commit(logits, masks, toks, phases, sh.block_size, wl.tau, wl.k_aggr,
+                             wl.mask_token_id)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    gbs = reps * (bytes_attn + bytes_commit) / el / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=int(blas), kind="oracle",
+                sample=(f"{reps} x (attention of layer 0 for query heads {heads[0]}..{heads[-1]} "
+                        f"of every request + commit pass over {rows} rows x "
+                        f"{wl.cfg['vocab']} logits), numpy fp64, {el:.1f} s; "
+                        f"host affinity {len(os.sched_getaffinity(0))} cpus"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the D2F step here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_causal_attention_d2f_amd as d2f
+    d2f.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K, Wu = args.steps, args.warmup
+    n_masks = Wu + K + args.call_reps + 1
+    wl = Workload(args.config, args.block_size, n_masks)
+    sh = wl.sh
+    use_graph = not args.no_graph
+
+    # One eager step first (it also proves the path runs) on a spare mask set.
+    wl.step(n_masks - 1)
+    torch.cuda.synchronize()
+
+    warm = capture(lambda: [wl.step(i) for i in range(Wu)], use_graph)
+    timed = capture(lambda: [wl.step(Wu + i) for i in range(K)], use_graph)
+    torch.cuda.synchronize()
+    warm()
+    torch.cuda.synchronize()
+    ms_total, wall_ms = time_region(timed)
+    ms_step = ms_total / K
+
+    calls = per_call_times(wl, args.call_reps, use_graph)
+    a_bytes = attn_bytes(sh)
+    a_flops = attn_flops(sh)
+    c_bytes = commit_bytes(wl.n_masked, wl.rows, wl.cfg["vocab"])
+    kv_b = kv_commit_bytes(sh, wl.layers)
+    t_attn = calls["d2f_block_attn"] * 1e-3
+    t_commit = calls["d2f_confidence_commit"] * 1e-3
+    t_kv = calls["d2f_kv_commit"] * 1e-3
+    attn_gbs = a_bytes / t_attn / 1e9
+    attn_tflops = a_flops / t_attn / 1e12
+    commit_gbs = c_bytes / t_commit / 1e9
+    shares = {"d2f_block_attn": t_attn * wl.layers, "d2f_confidence_commit": t_commit,
+              "d2f_kv_commit": t_kv}
+    dom = max(shares, key=shares.get)
+    ai = a_flops / a_bytes
+    if dom == "d2f_block_attn":
+        if ai * PEAK_HBM_GBS / 1e3 >= PEAK_BF16_TFLOPS:
+            roof = dict(kernel=dom, bound="mfma", achieved=round(attn_tflops, 3),
+                        peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+        else:
+            roof = dict(kernel=dom, bound="hbm", achieved=round(attn_gbs, 2), peak=PEAK_HBM_GBS,
+                        unit="GB/s")
+        per_launch = a_bytes
+    elif dom == "d2f_confidence_commit":
+        roof = dict(kernel=dom, bound="hbm", achieved=round(commit_gbs, 2), peak=PEAK_HBM_GBS,
+                    unit="GB/s")
+        per_launch = c_bytes
+    else:
+        roof = dict(kernel=dom, bound="hbm", achieved=round(kv_b / t_kv / 1e9, 2),
+                    peak=PEAK_HBM_GBS, unit="GB/s")
+        per_launch = kv_b
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["avg_us"] = round(shares[dom] / (wl.layers if dom == "d2f_block_attn" else 1) * 1e6, 3)
+    roof["algorithmic_bytes_per_launch"] = per_launch
+
+    step_bytes = wl.step_bytes()
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wu,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.cfg["workload"], "name": args.config, "batch": sh.batch,
+                   "heads_q": sh.n_heads_q, "heads_kv": sh.n_heads_kv, "head_dim": sh.head_dim,
+                   "block_size": sh.block_size, "prefix_len": (sh.prefix_len if sh.batch <= 4 else
+                                                               f"ragged, mean {sum(sh.prefix_len) / sh.batch:.0f}"),
+                   "n_win_blocks": (sh.n_win_blocks if sh.batch <= 4 else
+                                    f"ragged, {sum(sh.n_win_blocks)} blocks"),
+                   "layers": wl.layers, "vocab": wl.cfg["vocab"], "commit_rows": wl.rows,
+                   "tau": wl.tau, "input_sets": wl.n_sets,
+                   "input_set_bytes": wl.set_bytes,
+                   "launch": "hip-graph" if use_graph else "eager"},
+        "step_bytes": step_bytes,
+        "wall_ms_per_step": round(wall_ms / K, 5),
+        "attn": {"avg_us": round(t_attn * 1e6, 3), "tflops": round(attn_tflops, 3),
+                 "frac_mfma": round(attn_tflops / PEAK_BF16_TFLOPS, 5),
+                 "gbs": round(attn_gbs, 2), "frac_hbm": round(attn_gbs / PEAK_HBM_GBS, 4),
+                 "kv_read_gbs": round(attn_kv_bytes(sh) / t_attn / 1e9, 2),
+                 "flops": a_flops, "bytes": a_bytes, "intensity": round(ai, 2)},
+        "commit": {"avg_us": round(t_commit * 1e6, 3), "logit_gbs": round(commit_gbs, 2),
+                   "frac_hbm": round(commit_gbs / PEAK_HBM_GBS, 4), "bytes": c_bytes,
+                   "masked_rows": wl.n_masked},
+        "kv_commit": {"avg_us": round(t_kv * 1e6, 3), "gbs": round(kv_b / t_kv / 1e9, 2),
+                      "bytes": kv_b},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
