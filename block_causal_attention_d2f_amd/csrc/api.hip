@@ -1,6 +1,7 @@
 // C entry points of libd2f: argument checks, work planning and launches.
 // The operations themselves are documented in include/d2f.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -28,11 +29,41 @@ d2f_status_t hip_fail(hipError_t e, const char* what) {
   return fail(D2F_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Work-unit sizing: aim for this many workgroups per call (4 per CU on the
-// 256-CU part, enough to balance ragged key lengths), but never split a key
-// range into pieces shorter than kMinChunkTiles tiles.
-constexpr long long kTargetUnits = 1024;
+// Work-unit sizing.  The key tiles of all (request, KV head, query tile)
+// groups are cut into units of about C tiles, C = total tiles / (workgroups
+// resident on the device at once), so that one round of workgroups covers
+// the call: a second, mostly empty round would cost as much as the first.
+// Units never get shorter than kMinChunkTiles tiles.
 constexpr int kMinChunkTiles = 2;
+constexpr int kDefaultCUs = 256;        // MI355X, used when no device is visible
+constexpr int kDefaultWgsPerCU = 2;
+
+// Workgroups of the attention kernel resident at once on the current device.
+long long resident_workgroups(d2f_dtype_t dt, int head_dim) {
+  static std::atomic<int> cache[2][3];  // [dtype][head_dim 32/64/128] = resident WGs + 1
+  const int di = dt == D2F_BF16 ? 1 : 0;
+  const int hi = head_dim == 32 ? 0 : head_dim == 64 ? 1 : 2;
+  int v = cache[di][hi].load(std::memory_order_relaxed);
+  if (v > 0) return v - 1;
+  int dev = 0, cus = 0;
+  int per_cu = dt == D2F_BF16 ? attn_bf16_wgs_per_cu(head_dim) : attn_f32_wgs_per_cu(head_dim);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0 || per_cu <= 0) {
+    (void)hipGetLastError();  // no device visible: keep the MI355X defaults
+    cus = kDefaultCUs;
+    per_cu = kDefaultWgsPerCU;
+  }
+  v = cus * per_cu;
+  cache[di][hi].store(v + 1, std::memory_order_relaxed);
+  return v;
+}
+
+// Host copy of the kernel's visible-key end of query tile qt.
+long long host_tile_key_end(int qt, long long P, long long W, long long G, long long B) {
+  const long long r_last = std::min<long long>((qt + 1LL) * kQTile, G * W) - 1;
+  return P + std::min<long long>(W, ((r_last / G) / B + 1) * B);
+}
 
 bool head_dim_supported(d2f_dtype_t dt, int d) {
   if (dt == D2F_BF16) return d == 64 || d == 128;
@@ -87,56 +118,78 @@ struct Launch {
   std::vector<ReqInfo> req;
   int n_units = 0, n_groups = 0;
   bool any_split = false;
+  bool remap = false;
 };
 
+// Workspace of one launch: partial outputs, then partial (max, sum).
+size_t attn_partial_bytes(const Launch& L, int head_dim) {
+  return (size_t)L.n_units * kQTile * ((size_t)head_dim + 2) * sizeof(float);
+}
+
 // Split the batch into launches of at most kMaxReqPerLaunch requests and size
-// every request's key splits.  Returns the workspace bytes needed.
+// every request's key splits.  Within a launch, requests are ordered by unit
+// size, largest first, so that the short units fill in behind the long ones.
+// Returns the workspace bytes needed.
 size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
                       std::vector<Launch>& out) {
   const int G = d->n_heads_q / d->n_heads_kv;
+  const int B = d->block_size;
   long long total_tiles = 0;
   for (int b = 0; b < d->batch; ++b) {
-    const long long W = (long long)nwin[b] * d->block_size;
-    const long long qtiles = (G * W + kQTile - 1) / kQTile;
-    const long long keys = prefix[b] + W;
-    total_tiles += (long long)d->n_heads_kv * qtiles * ((keys + kKTile - 1) / kKTile);
+    const long long W = (long long)nwin[b] * B;
+    const int qtiles = (int)((G * W + kQTile - 1) / kQTile);
+    for (int qt = 0; qt < qtiles; ++qt)
+      total_tiles += (long long)d->n_heads_kv *
+                     ((host_tile_key_end(qt, prefix[b], W, G, B) + kKTile - 1) / kKTile);
   }
+  const long long slots = resident_workgroups(d->dtype, d->head_dim);
   const long long chunk_tiles =
-      std::max<long long>(kMinChunkTiles, (total_tiles + kTargetUnits - 1) / kTargetUnits);
+      std::max<long long>(kMinChunkTiles, (total_tiles + slots - 1) / slots);
   size_t ws = 0;
   out.clear();
   for (int b0 = 0; b0 < d->batch; b0 += kMaxReqPerLaunch) {
     Launch L;
     const int b1 = std::min(d->batch, b0 + kMaxReqPerLaunch);
+    std::vector<std::pair<long long, ReqInfo>> reqs;
     for (int b = b0; b < b1; ++b) {
       ReqInfo r{};
       r.b = b;
       r.prefix = prefix[b];
-      r.win = nwin[b] * d->block_size;
+      r.win = nwin[b] * B;
       r.qtiles = (G * r.win + kQTile - 1) / kQTile;
-      const long long tiles = (r.prefix + r.win + kKTile - 1) / kKTile;
-      r.nsplit = (int)((tiles + chunk_tiles - 1) / chunk_tiles);
-      if (r.nsplit <= 1) {
-        r.nsplit = 1;
-        r.chunk = (int)(tiles * kKTile);
-      } else {
-        r.chunk = (int)(chunk_tiles * kKTile);
-        L.any_split = true;
-      }
+      // The last query tile sees the most keys; it sets the split count.
+      const long long tiles =
+          (host_tile_key_end(r.qtiles - 1, r.prefix, r.win, G, B) + kKTile - 1) / kKTile;
+      r.nsplit = (int)std::max<long long>(1, (tiles + chunk_tiles - 1) / chunk_tiles);
+      if (r.nsplit > 1) L.any_split = true;
+      if (r.qtiles > 1) L.remap = true;
+      reqs.push_back({(tiles + r.nsplit - 1) / r.nsplit, r});
+    }
+    std::stable_sort(reqs.begin(), reqs.end(),
+                     [](const auto& x, const auto& y) { return x.first > y.first; });
+    for (auto& pr : reqs) {
+      ReqInfo r = pr.second;
       r.unit_base = L.n_units;
       r.group_base = L.n_groups;
       L.n_units += d->n_heads_kv * r.nsplit * r.qtiles;
       L.n_groups += d->n_heads_kv * r.qtiles;
       L.req.push_back(r);
     }
-    if (L.any_split)
-      ws = std::max(ws, (size_t)L.n_units * kQTile * ((size_t)d->head_dim + 2) * sizeof(float));
+    if (L.any_split) ws = std::max(ws, attn_partial_bytes(L, d->head_dim));
     out.push_back(std::move(L));
   }
   return ws;
 }
 
 size_t commit_chunks(int32_t vocab) { return (size_t)((vocab + kCommitChunk - 1) / kCommitChunk); }
+
+// Commit workspace: one (max, sum, argmax) partial per (row, chunk).
+size_t commit_partial_bytes(int32_t n_rows, int32_t vocab) {
+  return (size_t)n_rows * commit_chunks(vocab) * sizeof(float4);
+}
+size_t commit_workspace_bytes(int32_t n_rows, int32_t vocab) {
+  return commit_partial_bytes(n_rows, vocab);
+}
 
 }  // namespace
 }  // namespace d2f
@@ -231,6 +284,7 @@ d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const vo
     a.n_req = (int)L.req.size();
     a.n_units = L.n_units;
     a.n_groups = L.n_groups;
+    a.remap = L.remap ? 1 : 0;
     a.c2 = scale * 1.4426950408889634f;
     for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
     hipError_t e = desc->dtype == D2F_BF16 ? launch_attn_bf16(a, desc->head_dim, s)
@@ -300,7 +354,7 @@ d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
   if (bytes_out == nullptr) return fail(D2F_ERR_INVALID_ARG, "bytes_out is NULL");
   if (n_rows < 0 || vocab < 1)
     return fail(D2F_ERR_INVALID_ARG, "n_rows %d / vocab %d out of range", n_rows, vocab);
-  *bytes_out = (size_t)n_rows * commit_chunks(vocab) * sizeof(float4);
+  *bytes_out = commit_workspace_bytes(n_rows, vocab);
   return D2F_OK;
 }
 
@@ -326,7 +380,7 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
       n_committed == nullptr || block_complete == nullptr)
     return fail(D2F_ERR_INVALID_ARG, "a required pointer is NULL");
   const size_t n_chunks = commit_chunks(vocab);
-  const size_t need = (size_t)n_rows * n_chunks * sizeof(float4);
+  const size_t need = commit_workspace_bytes(n_rows, vocab);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                 workspace == nullptr ? (size_t)0 : workspace_bytes, need);

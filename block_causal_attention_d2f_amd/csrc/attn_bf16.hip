@@ -10,49 +10,72 @@
 //
 // Design (one workgroup = 4 waves = one work unit, see d2f_internal.h):
 //  * K and V tiles of 64 keys are staged HBM -> registers -> LDS with 16-byte
-//    coalesced loads, double-buffered so the next tile's loads are in flight
-//    while the current one is consumed.
+//    coalesced loads: two register sets and two LDS buffers keep the loads
+//    of the next two tiles in flight while the current one is consumed.
+//  * The LDS rows are unpadded and their 16-byte chunks XOR-swizzled by row,
+//    which makes both LDS read patterns below free of bank conflicts.
+//  * Wave w works on query rows [32 (w & 1), +32) -- two 16-row MFMA blocks --
+//    and on key half (w >> 1) -- 32 keys -- of every tile, so each K or V
+//    fragment read from LDS feeds two MFMAs and each wave runs two
+//    independent accumulation chains.  The two key halves are merged once,
+//    through LDS, at the end of the unit.
 //  * Scores are computed transposed, S^T = K Q^T: keys run along the MFMA M
-//    dimension and each wave's 16 query rows along N.  Each lane then holds
-//    one query and 4 keys per 16-key block, which is exactly the B operand
-//    layout (8 key slots per lane) of the next product O^T = V^T P^T, so
-//    probabilities go from accumulators to the PV MFMA without a shuffle.
-//  * V stays in its natural [key][dim] layout in LDS; the V^T operand is read
-//    with the gfx950 LDS transpose load (ds_read_b64_tr_b16).
-//  * Online softmax in base 2 with the scale folded into one multiply; row
-//    statistics are reduced across the 4 lanes holding one query.
+//    dimension and queries along N.  Each lane then holds one query and 8
+//    keys, exactly the B-operand layout of the next product O^T = V^T P^T,
+//    so probabilities go from accumulators to the PV MFMA without a shuffle.
+//    The V^T operand is read with the LDS transpose load ds_read_b64_tr_b16.
+//  * Online softmax in base 2: the row max is taken on raw scores and the
+//    scale is folded into the exp argument with one fma.  The reference max
+//    is raised lazily (only when a score exceeds it by 2^8), and each lane
+//    keeps its own partial sum, so the steady-state tile loop needs no
+//    cross-lane reduction at all.
 //  * A unit either covers all keys of its rows (writes O in bf16 and the LSE)
-//    or one key range (writes unnormalised O, running max and sum in fp32 for
-//    the merge kernel: the exact log-space composition of partial softmaxes).
+//    or one key range (writes unnormalised O, running max and sum in fp32,
+//    merged exactly by attn_merge.hip).
 #include "d2f_internal.h"
 
 namespace d2f {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+constexpr int kVmcntZero = 0x0F70;
+// Largest excess (base-2 units) of a score over the running reference max
+// before the reference is raised: probabilities stay below 2^kSlack.
+constexpr float kSlack = 8.0f;
+
+// Swizzle of 16-byte chunk positions within an LDS row.  Rows 0..7 map one
+// chunk to 8 different bank groups (K fragment reads: 8 rows, same chunk),
+// and for 4 consecutive rows starting at a multiple of 4 the chunk pairs
+// {2d, 2d+1} land on 8 different bank groups (V transpose reads).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
-  constexpr int S = D + 8;             // LDS row stride in bf16 (16-byte pad)
-  constexpr int KSTEPS = D / 32;       // MFMA k-steps over head_dim
-  constexpr int DBLK = D / 16;         // 16-dim blocks of the output
-  constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+  constexpr int RS = D * 2;                // LDS row bytes
+  constexpr int KSTEPS = D / 32;           // MFMA k-steps over head_dim
+  constexpr int DBLK = D / 16;             // 16-dim blocks of the output
+  constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
   constexpr int RPP = kAttnThreads / CPR;  // rows loaded per pass
   constexpr int PASSES = kKTile / RPP;
-  constexpr int TILE = kKTile * S;     // bf16 per K (or V) tile
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];  // [buf][K,V][key][dim]
+  constexpr int TILE = kKTile * RS;        // bytes per K (or V) tile
+  static_assert(PASSES == 2 || PASSES == 4, "loader covers 2 or 4 passes");
+  static_assert(2 * (2 * DBLK * 64 * 4 + 2 * 64 * 2) * 4 <= 4 * TILE, "merge area fits");
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [buf][K,V][key][dim]
 
-  const int u = xcd_remap(blockIdx.x, a.n_units);
+  const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
   const int rb = a.req[ri].b, P = a.req[ri].prefix, W = a.req[ri].win;
-  const int qtiles = a.req[ri].qtiles, nsplit = a.req[ri].nsplit, chunk = a.req[ri].chunk;
+  const int qtiles = a.req[ri].qtiles, nsplit = a.req[ri].nsplit;
   int local = u - a.req[ri].unit_base;
   const int qt = local % qtiles;
   local /= qtiles;
@@ -61,11 +84,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int G = a.group, B = a.bsz;
   const int rows = G * W;
   const int r0 = qt * kQTile;
-  const int r_last = min(r0 + kQTile, rows) - 1;
-  const int k_end = P + min(W, ((r_last / G) / B + 1) * B);   // last key any row sees
-  const int k_full = P + min(W, ((r0 / G) / B + 1) * B);      // keys every row sees
-  const int k_lo = split * chunk;
-  const int k_hi = min(k_lo + chunk, k_end);
+  const int k_end = tile_key_end(qt, P, W, G, B);          // last key any row sees
+  const int k_full = P + min(W, ((r0 / G) / B + 1) * B);  // keys every row sees
+  int k_lo, k_hi;
+  split_range(k_end, split, nsplit, k_lo, k_hi);
   const int n_tiles = k_hi > k_lo ? (k_hi - k_lo + kKTile - 1) / kKTile : 0;
   const int mask_from = min(k_full, k_hi);
 
@@ -79,173 +101,265 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 15, lg = lane >> 4;
+  const int qh = wave & 1, kh = wave >> 1;
 
-  // Loader mapping: 16-byte chunk c of rows n0 + RPP * p.
+  // Loader: 16-byte chunk ld_c of rows ld_n0 + RPP * p.  Rows past the
+  // unit's last key re-read the last valid key (branch-free, in bounds); the
+  // score mask gives them zero weight.
   const int ld_c = tid % CPR, ld_n0 = tid / CPR;
-  uint4 kreg[PASSES], vreg[PASSES];
-  auto gload = [&](int tile_lo) {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int j = tile_lo + ld_n0 + RPP * p;
-      if (j < k_hi) {
-        const __bf16* ks = (j < P) ? kc + (size_t)j * D : kw + (size_t)(j - P) * D;
-        const __bf16* vs = (j < P) ? vc + (size_t)j * D : vw + (size_t)(j - P) * D;
-        kreg[p] = *(const uint4*)(ks + 8 * ld_c);
-        vreg[p] = *(const uint4*)(vs + 8 * ld_c);
-      } else {
-        kreg[p] = make_uint4(0, 0, 0, 0);
-        vreg[p] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  auto ldk = [&](int p, int tile_lo) -> uint4 {
+    const int j = min(tile_lo + ld_n0 + RPP * p, k_hi - 1);
+    const __bf16* ks = (j < P) ? kc + (size_t)j * D : kw + (size_t)(j - P) * D;
+    return *(const uint4*)(ks + 8 * ld_c);
   };
-  auto lstore = [&](int buf) {
-    __bf16* kt = smem + buf * 2 * TILE;
-    __bf16* vt = kt + TILE;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int n = ld_n0 + RPP * p;
-      *(uint4*)(kt + n * S + 8 * ld_c) = kreg[p];
-      *(uint4*)(vt + n * S + 8 * ld_c) = vreg[p];
-    }
+  auto ldv = [&](int p, int tile_lo) -> uint4 {
+    const int j = min(tile_lo + ld_n0 + RPP * p, k_hi - 1);
+    const __bf16* vs = (j < P) ? vc + (size_t)j * D : vw + (size_t)(j - P) * D;
+    return *(const uint4*)(vs + 8 * ld_c);
   };
-
-  // This lane's query (MFMA column lc of this wave's 16 rows).
-  const int my_row = r0 + 16 * wave + lc;
-  const bool row_ok = my_row < rows;
-  const int my_i = row_ok ? my_row / G : 0;
-  const int my_h = kvh * G + (row_ok ? my_row % G : 0);
-  const int my_lim = min(k_hi, P + min(W, (my_i / B + 1) * B));
-  const bool wave_active = (r0 + 16 * wave) < rows;
-
-  bf16x8 qf[KSTEPS];
-  if (row_ok) {
-    const __bf16* qp = (const __bf16*)a.q + (((size_t)rb * a.hq + my_h) * a.wmax + my_i) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const bf16x8*)(qp + 32 * s + 8 * lg);
-  } else {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = bf16x8{};
+  auto st = [&](int p, int buf, uint4 kx, uint4 vx) {
+    const int n = ld_n0 + RPP * p;
+    char* kt = smem + buf * 2 * TILE + n * RS + ((ld_c ^ swz(n)) << 4);
+    *(uint4*)kt = kx;
+    *(uint4*)(kt + TILE) = vx;
+  };
+  uint4 ak0, ak1, ak2, ak3, av0, av1, av2, av3;
+  uint4 bk0, bk1, bk2, bk3, bv0, bv1, bv2, bv3;
+#define D2F_GLOAD(X, LO)                      \
+  {                                           \
+    X##k0 = ldk(0, LO); X##v0 = ldv(0, LO);   \
+    X##k1 = ldk(1, LO); X##v1 = ldv(1, LO);   \
+    if constexpr (PASSES > 2) {               \
+      X##k2 = ldk(2, LO); X##v2 = ldv(2, LO); \
+      X##k3 = ldk(3, LO); X##v3 = ldv(3, LO); \
+    }                                         \
+  }
+#define D2F_LSTORE(X, BUF)      \
+  {                             \
+    st(0, BUF, X##k0, X##v0);   \
+    st(1, BUF, X##k1, X##v1);   \
+    if constexpr (PASSES > 2) { \
+      st(2, BUF, X##k2, X##v2); \
+      st(3, BUF, X##k3, X##v3); \
+    }                           \
   }
 
-  f32x4 o[DBLK];
+  // This lane's two queries (MFMA column lc of the wave's two row blocks).
+  int my_i[2], my_h[2], my_lim[2];
+  bool row_ok[2];
+  bf16x8 qf[2][KSTEPS];
 #pragma unroll
-  for (int d = 0; d < DBLK; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = r0 + 32 * qh + 16 * qb + lc;
+    row_ok[qb] = row < rows;
+    my_i[qb] = row_ok[qb] ? row / G : 0;
+    my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
+    my_lim[qb] = min(k_hi, P + min(W, (my_i[qb] / B + 1) * B));
+    if (row_ok[qb]) {
+      const __bf16* qp =
+          (const __bf16*)a.q + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *(const bf16x8*)(qp + 32 * s + 8 * lg);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = bf16x8{};
+    }
+  }
+  const bool wave_active = (r0 + 32 * qh) < rows;
+  // Retire the Q loads here: left pending, they would make the first use in
+  // the tile loop wait on the in-order load counter every iteration, i.e. on
+  // the prefetched tiles too.
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+
+  f32x4 o[DBLK][2];
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
   const float c2 = a.c2;
 
-  if (n_tiles > 0) {
-    gload(k_lo);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const int tile_lo = k_lo + t * kKTile;
-    if (t + 1 < n_tiles) gload(tile_lo + kKTile);
-
-    if (wave_active) {
-      const __bf16* Ks = smem + buf * 2 * TILE;
-      const lds_bf16* Vs = (const lds_bf16*)(Ks + TILE);
-      f32x4 sc[4];
+  auto compute = [&](int buf, int tile_lo) {
+    const char* Ks = smem + buf * 2 * TILE;
+    const lds_char* Vs = (const lds_char*)(Ks + TILE);
+    // S^T for this wave's 32 keys x 32 queries: [key block][query block].
+    f32x4 sc[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int n = 32 * kh + 16 * kb + lc;
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 ka = *(const bf16x8*)(Ks + (16 * kb + lc) * S + 32 * s + 8 * lg);
-          sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[s], sc[kb], 0, 0, 0);
-        }
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + n * RS + (((4 * s + lg) ^ swz(n)) << 4));
+        sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[0][s], sc[kb][0], 0, 0, 0);
+        sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[1][s], sc[kb][1], 0, 0, 0);
       }
-      // Scale, mask, and the row maximum of this tile.
-      const bool need_mask = tile_lo + kKTile > mask_from;
+    }
+    const int key0 = tile_lo + 32 * kh + 4 * lg;  // key of sc[0][*][0]
+    const bool need_mask = tile_lo + kKTile > mask_from;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = sc[kb][r] * c2;
-          if (need_mask && tile_lo + 16 * kb + 4 * lg + r >= my_lim) x = kNegInf;
-          sc[kb][r] = x;
-          mx = fmaxf(mx, x);
+          if (need_mask && key0 + 16 * kb + r >= my_lim[qb]) sc[kb][qb][r] = kNegInf;
+          mx = fmaxf(mx, sc[kb][qb][r]);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // Lazy rescaling: the reference max m_run only moves when some score
+      // exceeds it by more than kSlack (base-2 units), so in the steady state
+      // no cross-lane reduction is needed; probabilities then stay <= 2^kSlack.
+      if (__any(mx * c2 > m_run[qb] + kSlack)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx * c2);
+        const float alpha = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) o[d][qb] *= alpha;
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
       float ps = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sc[kb][r] - m_use);
-          sc[kb][r] = p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r], c2, -m_use));
           ps += p;
+          pf[qb][4 * kb + r] = (__bf16)p;
         }
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d) o[d] *= alpha;
-
-      // O^T += V^T P^T over two 32-key halves of the tile.
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        bf16x8 pf;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pf[r] = (__bf16)sc[2 * kh][r];
-          pf[4 + r] = (__bf16)sc[2 * kh + 1][r];
-        }
-        const lds_bf16* vrow = Vs + (32 * kh + 4 * lg + (lc >> 2)) * S + 4 * (lc & 3);
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d) {
-          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + 16 * d));
-          const i16x4 t1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vrow + 16 * S + 16 * d));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-          o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf,
-                                                          o[d], 0, 0, 0);
-        }
-      }
+      l_run[qb] += ps;  // this lane's keys only; lanes are summed once at the end
     }
-
-    if (t + 1 < n_tiles) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (!wave_active || !row_ok) return;
-  if (nsplit == 1) {
-    const float inv = 1.0f / l_run;
-    __bf16* op = (__bf16*)a.out + (((size_t)rb * a.hq + my_h) * a.wmax + my_i) * D;
+    // O^T += V^T P^T over this wave's 32 keys.  Lane (lc, lg) of the
+    // transposed read gets V[key 32kh + 4lg + e][dim 16d + lc] for e < 4
+    // (and +16 keys from the second read): k-slots 8lg..8lg+7 in the same
+    // key order as the lane's probabilities.
+    const int vr = 32 * kh + 4 * lg + (lc >> 2);
+    const int vbyte = (lc & 1) << 3;
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[d][r] * inv);
-      *(bf16x4*)(op + 16 * d + 4 * lg) = v;
+      const int cidx = 2 * d + ((lc & 3) >> 1);
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz(vr)) << 4) + vbyte));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz(vr + 16)) << 4) + vbyte));
+      const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, both);
+      o[d][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[0], o[d][0], 0, 0, 0);
+      o[d][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[1], o[d][1], 0, 0, 0);
     }
-    if (a.lse != nullptr && lg == 0)
-      a.lse[((size_t)rb * a.hq + my_h) * a.wmax + my_i] = (m_run + log2f(l_run)) * kLn2;
-  } else {
-    const size_t row_slot = (size_t)u * kQTile + 16 * wave + lc;
-    float* wp = a.ws_o + row_slot * D;
+  };
+
+  // Loads and LDS stores are issued unconditionally so that the compiler can
+  // count exactly which loads each wait covers; past the last tile they
+  // re-read the last tile (cache hits) and fill a buffer nobody reads.
+  if (n_tiles > 0) {
+    const int last_lo = k_lo + (n_tiles - 1) * kKTile;
+    auto tile_at = [&](int t) { return min(k_lo + t * kKTile, last_lo); };
+    D2F_GLOAD(a, tile_at(0));
+    D2F_GLOAD(b, tile_at(1));
+    D2F_LSTORE(a, 0);
+    __syncthreads();
+    // Pairs of tiles; entering each pair, buffer 0 holds tile t and set b
+    // carries tile t+1.  One back-edge and one exit keep the compiler's
+    // load-counter bookkeeping exact.
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      D2F_GLOAD(a, tile_at(t + 2));
+      if (wave_active) compute(0, k_lo + t * kKTile);
+      D2F_LSTORE(b, 1);
+      __syncthreads();
+      D2F_GLOAD(b, tile_at(t + 3));
+      if (wave_active) compute(1, k_lo + (t + 1) * kKTile);
+      D2F_LSTORE(a, 0);
+      __syncthreads();
+    }
+    if (t < n_tiles && wave_active) compute(0, k_lo + t * kKTile);  // odd tail
+  }
+#undef D2F_GLOAD
+#undef D2F_LSTORE
+
+  // Per-lane partial sums to per-query sums (the 4 lanes of a query column).
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d) *(f32x4*)(wp + 16 * d + 4 * lg) = o[d];
-    if (lg == 0) {
-      a.ws_ml[row_slot * 2 + 0] = m_run;
-      a.ws_ml[row_slot * 2 + 1] = l_run;
+  for (int qb = 0; qb < 2; ++qb) {
+    l_run[qb] += __shfl_xor(l_run[qb], 16);
+    l_run[qb] += __shfl_xor(l_run[qb], 32);
+  }
+
+  // Merge the two key halves: the wave of key half 1 hands (m, l, O) to the
+  // wave of key half 0 with the same query half through LDS (same lane,
+  // same register layout).
+  __syncthreads();  // tile buffers are free from here on
+  float* xo = (float*)smem + (size_t)qh * (2 * DBLK * 64 * 4);  // [qb][d][lane][4]
+  float* xml = (float*)smem + 2 * (2 * DBLK * 64 * 4) + qh * (2 * 64 * 2);
+  if (kh == 1 && wave_active) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) = o[d][qb];
+      xml[(qb * 64 + lane) * 2 + 0] = m_run[qb];
+      xml[(qb * 64 + lane) * 2 + 1] = l_run[qb];
+    }
+  }
+  __syncthreads();
+  if (kh == 1 || !wave_active) return;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float m1 = xml[(qb * 64 + lane) * 2 + 0], l1 = xml[(qb * 64 + lane) * 2 + 1];
+    const float m = fmaxf(m_run[qb], m1);
+    const float w0 = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+    const float w1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+      o[d][qb] = o[d][qb] * w0 + *(const f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) * w1;
+    l_run[qb] = l_run[qb] * w0 + l1 * w1;
+    m_run[qb] = m;
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!row_ok[qb]) continue;
+    if (nsplit == 1) {
+      const float inv = 1.0f / l_run[qb];
+      __bf16* op =
+          (__bf16*)a.out + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[d][qb][r] * inv);
+        *(bf16x4*)(op + 16 * d + 4 * lg) = v;
+      }
+      if (a.lse != nullptr && lg == 0)
+        a.lse[((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]] =
+            (m_run[qb] + log2f(l_run[qb])) * kLn2;
+    } else {
+      const size_t row_slot = (size_t)u * kQTile + 32 * qh + 16 * qb + lc;
+      float* wp = a.ws_o + row_slot * D;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) *(f32x4*)(wp + 16 * d + 4 * lg) = o[d][qb];
+      if (lg == 0) {
+        a.ws_ml[row_slot * 2 + 0] = m_run[qb];
+        a.ws_ml[row_slot * 2 + 1] = l_run[qb];
+      }
     }
   }
 }
 
 }  // namespace
+
+int attn_bf16_wgs_per_cu(int head_dim) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  if (head_dim == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128>, kAttnThreads, 0);
+  else if (head_dim == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64>, kAttnThreads, 0);
+  return e == hipSuccess ? n : 0;
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.n_units), block(kAttnThreads);

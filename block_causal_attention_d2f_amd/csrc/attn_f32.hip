@@ -26,10 +26,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   __shared__ float Vs[kKTile][D];
   __shared__ float Ps[kQTile][kKTile + 1];
 
-  const int u = xcd_remap(blockIdx.x, a.n_units);
+  const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
   const int rb = a.req[ri].b, P = a.req[ri].prefix, W = a.req[ri].win;
-  const int qtiles = a.req[ri].qtiles, nsplit = a.req[ri].nsplit, chunk = a.req[ri].chunk;
+  const int qtiles = a.req[ri].qtiles, nsplit = a.req[ri].nsplit;
   int local = u - a.req[ri].unit_base;
   const int qt = local % qtiles;
   local /= qtiles;
@@ -38,10 +38,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const int G = a.group, B = a.bsz;
   const int rows = G * W;
   const int r0 = qt * kQTile;
-  const int r_last = min(r0 + kQTile, rows) - 1;
-  const int k_end = P + min(W, ((r_last / G) / B + 1) * B);
-  const int k_lo = split * chunk;
-  const int k_hi = min(k_lo + chunk, k_end);
+  const int k_end = tile_key_end(qt, P, W, G, B);
+  int k_lo, k_hi;
+  split_range(k_end, split, nsplit, k_lo, k_hi);
   const int n_tiles = k_hi > k_lo ? (k_hi - k_lo + kKTile - 1) / kKTile : 0;
 
   const size_t head_c = ((size_t)rb * a.hkv + kvh) * (size_t)a.cap * D;
@@ -130,15 +129,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
     }
   }
 
-  if (!row_ok) return;
   if (nsplit == 1) {
+    if (!row_ok) return;
     const float inv = 1.0f / l_run;
     float* op = (float*)a.out + (((size_t)rb * a.hq + my_h) * a.wmax + my_i) * D;
 #pragma unroll
     for (int k = 0; k < D / 4; ++k) op[sub + 4 * k] = acc[k] * inv;
     if (a.lse != nullptr && sub == 0)
       a.lse[((size_t)rb * a.hq + my_h) * a.wmax + my_i] = (m_run + log2f(l_run)) * kLn2;
-  } else {
+    return;
+  }
+  if (row_ok) {
     const size_t row_slot = (size_t)u * kQTile + r;
     float* wp = a.ws_o + row_slot * D;
 #pragma unroll
@@ -151,6 +152,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
 }
 
 }  // namespace
+
+int attn_f32_wgs_per_cu(int head_dim) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (head_dim) {
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<32>, kAttnThreads, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<64>, kAttnThreads, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_f32_kernel<128>, kAttnThreads, 0); break;
+    default: break;
+  }
+  return e == hipSuccess ? n : 0;
+}
 
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.n_units), block(kAttnThreads);

@@ -7,19 +7,21 @@
 // 조기 확정 디코딩(Prophet)": the confidence is the maximum softmax
 // probability, and "양방향 어텐션과 사라진 KV 캐시": low-confidence remasking.
 //
-// Kernel 1 (vocab_reduce) streams each MASKED row once from HBM.  A row is
-// cut into chunks of 8192 logits, one workgroup per (row, chunk); every
-// thread loads its 32 values with 16-byte loads, forms its own (max, first
-// argmax, sum of exp(x - max)), and the workgroup combines them with 64-wide
-// wavefront shuffles and a fixed-order cross-wave step.  Rows already
-// COMMITTED are skipped without reading their logits.
+// Kernel 1 (vocab_reduce): one workgroup per (row, chunk of 8192 logits).  A
+// MASKED row's chunk is streamed once from HBM with 16-byte loads (8 per
+// thread, all in flight together); every thread takes the max of its 32
+// values and the sum of exp(x - max), the workgroup reduces the max,
+// rescales and reduces the sums (wavefront shuffles, then a fixed-order
+// cross-wave step), and the threads holding the maximum agree on its first
+// index.  COMMITTED rows are not read.
 //
-// Kernel 2 (commit_decide), one wavefront per D2F block, merges a row's
-// chunk partials in chunk order, takes conf = 1 / sum (the max term is
-// exp(0) = 1), compares with the float threshold, ranks the block's masked
-// rows for the aggressive top-k (ties to the lower position), and writes the
-// new mask state, tokens and per-block counts.  No floating-point atomics:
-// the result is deterministic.
+// Kernel 2 (commit_decide): one workgroup per D2F block.  The block's chunk
+// partials are staged through LDS 256 at a time (one load per thread, so a
+// block needs a handful of memory round trips), each row merges its partials
+// in chunk order, conf = 1 / sum (the max term is exp(0) = 1) is compared with
+// the threshold, the aggressive top-k ranks the block's masked rows (ties to
+// the lower position), and the new mask state, tokens and per-block counts
+// are written.  No floating-point atomics: results are deterministic.
 #include <climits>
 
 #include "d2f_internal.h"
@@ -29,147 +31,183 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct Part {
-  float m;  // running max
-  float s;  // sum of exp(x - m)
-  int i;    // first index attaining m
-};
-
-__device__ __forceinline__ Part combine(Part a, Part b) {
-  Part r;
-  r.m = fmaxf(a.m, b.m);
-  r.i = (a.m > b.m) ? a.i : (b.m > a.m) ? b.i : min(a.i, b.i);
-  if (r.m == kNegInf) {
-    r.s = 0.f;
-  } else {
-    r.s = a.s * __builtin_amdgcn_exp2f((a.m - r.m) * kLog2e) +
-          b.s * __builtin_amdgcn_exp2f((b.m - r.m) * kLog2e);
-  }
-  return r;
-}
-
-__device__ __forceinline__ Part shfl_xor_part(Part p, int o) {
-  Part q;
-  q.m = __shfl_xor(p.m, o);
-  q.s = __shfl_xor(p.s, o);
-  q.i = __shfl_xor(p.i, o);
-  return q;
-}
-
 constexpr int kPerThread = kCommitChunk / kCommitThreads;  // 32 logits per thread
+constexpr int kWaves = kCommitThreads / 64;
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Merge two (max, sum, first index) partials of disjoint index ranges.
+__device__ __forceinline__ void combine(float& m, float& s, int& i, float m2, float s2, int i2) {
+  const float mm = fmaxf(m, m2);
+  const int ii = (m > m2) ? i : (m2 > m) ? i2 : min(i, i2);
+  float ss = 0.f;
+  if (mm != kNegInf)
+    ss = s * __builtin_amdgcn_exp2f((m - mm) * kLog2e) + s2 * __builtin_amdgcn_exp2f((m2 - mm) * kLog2e);
+  m = mm;
+  s = ss;
+  i = ii;
+}
+
+// Reduce one chunk of one row; returns (max, sum, first argmax) in thread 0.
 template <bool VEC>
-__global__ __launch_bounds__(kCommitThreads) void vocab_reduce_kernel(const CommitArgs a) {
-  const int row = blockIdx.x / a.n_chunks;
-  const int ck = blockIdx.x - row * a.n_chunks;
-  if (a.mask_state[row] != D2F_MASKED) return;
+__device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& result) {
+  __shared__ float sh_m[kWaves], sh_s[kWaves];
+  __shared__ int sh_i;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = ck * kCommitChunk;
   const int n = min(kCommitChunk, a.vocab - c0);
   const float* src = a.logits + (size_t)row * a.ld + c0;
-  const int tid = threadIdx.x;
 
+  // x[4k + c] is logit 4 * (tid + 256 k) + c (vector path) or tid + 256 k.
   float x[kPerThread];
-  int base[kPerThread];  // chunk-relative index of x[e]
-  if (VEC) {
-    // float4 number q = tid + 256 * k covers logits 4q .. 4q + 3.
+  if (VEC && n == kCommitChunk) {
+#pragma unroll
+    for (int k = 0; k < kPerThread / 4; ++k) {
+      const float4 v = *(const float4*)(src + 4 * (tid + kCommitThreads * k));
+      x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
+    }
+  } else if (VEC) {
 #pragma unroll
     for (int k = 0; k < kPerThread / 4; ++k) {
       const int e0 = 4 * (tid + kCommitThreads * k);
-      float4 v;
       if (e0 + 3 < n) {
-        v = *(const float4*)(src + e0);
+        const float4 v = *(const float4*)(src + e0);
+        x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
       } else {
-        v.x = (e0 + 0 < n) ? src[e0 + 0] : kNegInf;
-        v.y = (e0 + 1 < n) ? src[e0 + 1] : kNegInf;
-        v.z = (e0 + 2 < n) ? src[e0 + 2] : kNegInf;
-        v.w = (e0 + 3 < n) ? src[e0 + 3] : kNegInf;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[4 * k + c] = (e0 + c < n) ? src[e0 + c] : kNegInf;
       }
-      x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
-      base[4 * k + 0] = e0; base[4 * k + 1] = e0 + 1; base[4 * k + 2] = e0 + 2;
-      base[4 * k + 3] = e0 + 3;
     }
   } else {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int e = tid + kCommitThreads * k;
       x[k] = (e < n) ? src[e] : kNegInf;
-      base[k] = e;
     }
   }
-  // Thread-local max and first argmax (x[] is in increasing index order).
-  Part p;
-  p.m = kNegInf;
-  p.i = INT_MAX;
+  float m = kNegInf;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    if (x[k] > p.m) {
-      p.m = x[k];
-      p.i = c0 + base[k];
+  for (int k = 0; k < kPerThread; ++k) m = fmaxf(m, x[k]);
+  // exp(x - m) as 2^((x - m) log2 e): the difference is exact for the terms
+  // near the maximum that dominate the sum, so their relative error stays at
+  // a few ulp (folding m * log2 e into one fma would shift every term of the
+  // thread by the rounding of that product instead).
+  float s = 0.f;
+  if (m != kNegInf) {
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) s += __builtin_amdgcn_exp2f((x[k] - m) * kLog2e);
+  }
+  // Workgroup maximum.
+  const float wm = wave_max(m);
+  if (lane == 0) sh_m[wave] = wm;
+  if (tid == 0) sh_i = INT_MAX;
+  __syncthreads();
+  float M = sh_m[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh_m[w]);
+  // First index of the maximum: only threads holding it search.
+  if (m == M && M != kNegInf) {
+    int first = INT_MAX;
+#pragma unroll
+    for (int k = kPerThread - 1; k >= 0; --k) {
+      const int idx = VEC ? 4 * (tid + kCommitThreads * (k >> 2)) + (k & 3)
+                          : tid + kCommitThreads * k;
+      if (x[k] == M) first = idx;
     }
+    atomicMin(&sh_i, c0 + first);  // integer minimum: order-independent
   }
-  p.s = 0.f;
-  if (p.m != kNegInf) {
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) p.s += __builtin_amdgcn_exp2f((x[k] - p.m) * kLog2e);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) p = combine(p, shfl_xor_part(p, o));
-
-  __shared__ Part wp[kCommitThreads / 64];
-  if ((tid & 63) == 0) wp[tid >> 6] = p;
+  // Sums rescaled to the workgroup maximum, then reduced in a fixed order.
+  const float sr = (M == kNegInf || m == kNegInf) ? 0.f
+                                                  : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  const float ws = wave_sum(sr);
+  if (lane == 0) sh_s[wave] = ws;
   __syncthreads();
   if (tid == 0) {
-    Part t = wp[0];
+    float S = sh_s[0];
 #pragma unroll
-    for (int w = 1; w < kCommitThreads / 64; ++w) t = combine(t, wp[w]);
-    a.partial[(size_t)row * a.n_chunks + ck] = make_float4(t.m, t.s, __int_as_float(t.i), 0.f);
+    for (int w = 1; w < kWaves; ++w) S += sh_s[w];
+    result = make_float4(M, S, __int_as_float(sh_i), 0.f);
   }
 }
 
-__global__ __launch_bounds__(64) void commit_decide_kernel(const CommitArgs a) {
+constexpr int kRowsPerThread = kMaxCommitBlock / kCommitThreads;  // 4
+
+__global__ __launch_bounds__(kCommitThreads) void commit_decide_kernel(const CommitArgs a) {
   __shared__ float s_conf[kMaxCommitBlock];
   __shared__ int s_idx[kMaxCommitBlock];
   __shared__ unsigned char s_live[kMaxCommitBlock];
-  const int k = blockIdx.x;
-  const int B = a.block_size;
-  const size_t row0 = (size_t)k * B;
+  __shared__ float4 s_stage[kCommitThreads];
+  __shared__ int s_cnt, s_incomplete;
+  const int blk = blockIdx.x;
+  const int B = a.block_size, nck = a.n_chunks;
+  const size_t row0 = (size_t)blk * B;
   const int tid = threadIdx.x;
-
-  for (int p = tid; p < B; p += 64) {
-    const size_t row = row0 + p;
-    const bool live = a.mask_state[row] == D2F_MASKED;
-    float conf = 0.f;
-    int idx = -1;
-    if (live) {
-      const float4* pp = a.partial + row * a.n_chunks;
-      float4 v = pp[0];
-      Part t{v.x, v.y, __float_as_int(v.z)};
-      for (int c = 1; c < a.n_chunks; ++c) {
-        v = pp[c];
-        t = combine(t, Part{v.x, v.y, __float_as_int(v.z)});
-      }
-      conf = 1.0f / t.s;
-      idx = t.i;
-    }
-    s_conf[p] = conf;
-    s_idx[p] = idx;
-    s_live[p] = live ? 1 : 0;
+  if (tid == 0) {
+    s_cnt = 0;
+    s_incomplete = 0;
+  }
+  for (int p = tid; p < B; p += kCommitThreads) s_live[p] = a.mask_state[row0 + p] == D2F_MASKED;
+  // Running (max, sum, index) of rows tid, tid + 256, ... (chunk order).
+  float rm[kRowsPerThread], rs[kRowsPerThread];
+  int ri[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    rm[k] = kNegInf;
+    rs[k] = 0.f;
+    ri[k] = INT_MAX;
   }
   __syncthreads();
-
-  const bool aggressive = a.block_phase[k] == D2F_AGGRESSIVE && a.k_aggr > 0;
-  int cnt = 0;
-  int incomplete = 0;
-  for (int p = tid; p < B; p += 64) {
+  const int total = B * nck;  // partials of the block, row-major [row][chunk]
+  for (int base = 0; base < total; base += kCommitThreads) {
+    const int e = base + tid;
+    if (e < total && s_live[e / nck]) s_stage[tid] = a.partial[row0 * nck + e];
+    __syncthreads();
+    const int hi = min(total, base + kCommitThreads);
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int p = tid + k * kCommitThreads;
+      if (p >= B || !s_live[p]) continue;
+      const int c_lo = max(base, p * nck), c_hi = min(hi, (p + 1) * nck);
+      for (int c = c_lo; c < c_hi; ++c) {
+        const float4 v = s_stage[c - base];
+        if (c == p * nck) {
+          rm[k] = v.x;
+          rs[k] = v.y;
+          ri[k] = __float_as_int(v.z);
+        } else {
+          combine(rm[k], rs[k], ri[k], v.x, v.y, __float_as_int(v.z));
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int p = tid + k * kCommitThreads;
+    if (p >= B) continue;
+    s_conf[p] = s_live[p] ? 1.0f / rs[k] : 0.f;
+    s_idx[p] = s_live[p] ? ri[k] : -1;
+  }
+  __syncthreads();
+  const bool aggressive = a.block_phase[blk] == D2F_AGGRESSIVE && a.k_aggr > 0;
+  int cnt = 0, incomplete = 0;
+  for (int p = tid; p < B; p += kCommitThreads) {
     if (!s_live[p]) continue;
     const float c = s_conf[p];
     bool commit = c > a.tau;
     if (!commit && aggressive) {
       int rank = 0;
-      for (int q = 0; q < B && rank < a.k_aggr; ++q) {
+      for (int q = 0; q < B && rank < a.k_aggr; ++q)
         if (s_live[q] && (s_conf[q] > c || (s_conf[q] == c && q < p))) ++rank;
-      }
       commit = rank < a.k_aggr;
     }
     const size_t row = row0 + p;
@@ -184,32 +222,40 @@ __global__ __launch_bounds__(64) void commit_decide_kernel(const CommitArgs a) {
       incomplete = 1;
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    cnt += __shfl_xor(cnt, o);
-    incomplete |= __shfl_xor(incomplete, o);
-  }
+  if (cnt) atomicAdd(&s_cnt, cnt);            // integer: order-independent
+  if (incomplete) atomicOr(&s_incomplete, 1);
+  __syncthreads();
   if (tid == 0) {
-    a.n_committed[k] = cnt;
-    a.block_complete[k] = incomplete ? 0 : 1;
+    a.n_committed[blk] = s_cnt;
+    a.block_complete[blk] = s_incomplete ? 0 : 1;
   }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kCommitThreads) void vocab_reduce_kernel(const CommitArgs a) {
+  const int row = blockIdx.x / a.n_chunks;
+  const int ck = blockIdx.x - row * a.n_chunks;
+  if (a.mask_state[row] != D2F_MASKED) return;
+  float4 part;
+  reduce_chunk<VEC>(a, row, ck, part);
+  if (threadIdx.x == 0) a.partial[(size_t)row * a.n_chunks + ck] = part;
 }
 
 }  // namespace
 
 hipError_t launch_confidence_commit(const CommitArgs& a, bool vec4, hipStream_t s) {
-  const int n_blocks = a.n_rows / a.block_size;
-  if (n_blocks == 0) return hipSuccess;
-  const long long grid1 = (long long)a.n_rows * a.n_chunks;
+  if (a.n_rows == 0) return hipSuccess;
+  const long long grid = (long long)a.n_rows * a.n_chunks;
   if (vec4)
-    hipLaunchKernelGGL(vocab_reduce_kernel<true>, dim3((unsigned)grid1), dim3(kCommitThreads), 0,
-                       s, a);
+    hipLaunchKernelGGL(vocab_reduce_kernel<true>, dim3((unsigned)grid), dim3(kCommitThreads), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL(vocab_reduce_kernel<false>, dim3((unsigned)grid1), dim3(kCommitThreads), 0,
+    hipLaunchKernelGGL(vocab_reduce_kernel<false>, dim3((unsigned)grid), dim3(kCommitThreads), 0,
                        s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_decide_kernel, dim3(n_blocks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(commit_decide_kernel, dim3(a.n_rows / a.block_size), dim3(kCommitThreads), 0,
+                     s, a);
   return hipGetLastError();
 }
 

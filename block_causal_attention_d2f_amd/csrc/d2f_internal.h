@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/d2f.h"
+#include "d2f.h"
 
 namespace d2f {
 
@@ -24,10 +24,10 @@ struct ReqInfo {
   int32_t prefix;     // P: cached tokens
   int32_t win;        // W: window tokens (n_win_blocks * block_size)
   int32_t qtiles;     // ceil(group * W / kQTile)
-  int32_t nsplit;     // key-range splits (1 = the unit writes final outputs)
-  int32_t chunk;      // keys per split, a multiple of kKTile
+  int32_t nsplit;     // key-range splits per query tile (1 = final outputs)
   int32_t unit_base;  // first work unit of this request within the launch
   int32_t group_base; // first (kv_head, qtile) merge group within the launch
+  int32_t reserved;
 };
 
 struct AttnArgs {
@@ -43,7 +43,8 @@ struct AttnArgs {
   int64_t cap;   // cache slots per (request, KV head)
   int32_t hq, hkv, group, wmax, bsz;
   int32_t n_req, n_units, n_groups;
-  float c2;      // softmax scale * log2(e)
+  int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
+  float c2;       // softmax scale * log2(e)
   ReqInfo req[kMaxReqPerLaunch];
 };
 
@@ -66,6 +67,20 @@ __device__ __forceinline__ int find_req_group(const AttnArgs& a, int g) {
   return lo;
 }
 
+// Visible-key end of query tile qt: the last row's window block bounds it.
+__device__ __forceinline__ int tile_key_end(int qt, int P, int W, int G, int B) {
+  const int r_last = min((qt + 1) * kQTile, G * W) - 1;
+  return P + min(W, ((r_last / G) / B + 1) * B);
+}
+
+// Key range of split s of a query tile whose visible keys end at k_end: the
+// tile's ceil(k_end / kKTile) key tiles are divided as evenly as possible.
+__device__ __forceinline__ void split_range(int k_end, int s, int nsplit, int& k_lo, int& k_hi) {
+  const int nt = (k_end + kKTile - 1) / kKTile;
+  k_lo = (s * nt / nsplit) * kKTile;
+  k_hi = min(((s + 1) * nt / nsplit) * kKTile, k_end);
+}
+
 // Workgroups are dealt round-robin over the 8 XCDs (workgroup x runs on XCD
 // x % 8).  Renumber so that each XCD receives a contiguous run of logical
 // units: neighbouring units (the query tiles of one KV range) then share that
@@ -78,6 +93,9 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
+// Attention workgroups that fit on one CU at once (0 if unknown).
+int attn_bf16_wgs_per_cu(int head_dim);
+int attn_f32_wgs_per_cu(int head_dim);
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, d2f_dtype_t dt, hipStream_t s);
 
 struct CommitArgs {
