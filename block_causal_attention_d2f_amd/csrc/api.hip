@@ -126,6 +126,11 @@ size_t attn_partial_bytes(const Launch& L, int head_dim) {
   return (size_t)L.n_units * kQTile * ((size_t)head_dim + 2) * sizeof(float);
 }
 
+// Host copy of the kernels' key-tile count: cache and window tiled apart.
+long long host_key_tiles(long long P, long long k_end) {
+  return (P + kKTile - 1) / kKTile + (k_end - P + kKTile - 1) / kKTile;
+}
+
 // Split the batch into launches of at most kMaxReqPerLaunch requests and size
 // every request's key splits.  Within a launch, requests are ordered by unit
 // size, largest first, so that the short units fill in behind the long ones.
@@ -140,7 +145,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
     const int qtiles = (int)((G * W + kQTile - 1) / kQTile);
     for (int qt = 0; qt < qtiles; ++qt)
       total_tiles += (long long)d->n_heads_kv *
-                     ((host_tile_key_end(qt, prefix[b], W, G, B) + kKTile - 1) / kKTile);
+                     host_key_tiles(prefix[b], host_tile_key_end(qt, prefix[b], W, G, B));
   }
   const long long slots = resident_workgroups(d->dtype, d->head_dim);
   const long long chunk_tiles =
@@ -159,7 +164,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
       r.qtiles = (G * r.win + kQTile - 1) / kQTile;
       // The last query tile sees the most keys; it sets the split count.
       const long long tiles =
-          (host_tile_key_end(r.qtiles - 1, r.prefix, r.win, G, B) + kKTile - 1) / kKTile;
+          host_key_tiles(r.prefix, host_tile_key_end(r.qtiles - 1, r.prefix, r.win, G, B));
       r.nsplit = (int)std::max<long long>(1, (tiles + chunk_tiles - 1) / chunk_tiles);
       if (r.nsplit > 1) L.any_split = true;
       if (r.qtiles > 1) L.remap = true;

@@ -86,10 +86,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int r0 = qt * kQTile;
   const int k_end = tile_key_end(qt, P, W, G, B);          // last key any row sees
   const int k_full = P + min(W, ((r0 / G) / B + 1) * B);  // keys every row sees
-  int k_lo, k_hi;
-  split_range(k_end, split, nsplit, k_lo, k_hi);
-  const int n_tiles = k_hi > k_lo ? (k_hi - k_lo + kKTile - 1) / kKTile : 0;
-  const int mask_from = min(k_full, k_hi);
+  const int nct = cache_tiles(P);
+  int t_lo, t_hi;
+  split_tiles(nct + window_tiles(P, k_end), split, nsplit, t_lo, t_hi);
+  const int n_tiles = t_hi - t_lo;
 
   const size_t head_c = ((size_t)rb * a.hkv + kvh) * (size_t)a.cap * D;
   const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
@@ -103,36 +103,45 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int lc = lane & 15, lg = lane >> 4;
   const int qh = wave & 1, kh = wave >> 1;
 
-  // Loader: 16-byte chunk ld_c of rows ld_n0 + RPP * p.  Rows past the
-  // unit's last key re-read the last valid key (branch-free, in bounds); the
-  // score mask gives them zero weight.
-  const int ld_c = tid % CPR, ld_n0 = tid / CPR;
-  auto ldk = [&](int p, int tile_lo) -> uint4 {
-    const int j = min(tile_lo + ld_n0 + RPP * p, k_hi - 1);
-    const __bf16* ks = (j < P) ? kc + (size_t)j * D : kw + (size_t)(j - P) * D;
-    return *(const uint4*)(ks + 8 * ld_c);
-  };
-  auto ldv = [&](int p, int tile_lo) -> uint4 {
-    const int j = min(tile_lo + ld_n0 + RPP * p, k_hi - 1);
-    const __bf16* vs = (j < P) ? vc + (size_t)j * D : vw + (size_t)(j - P) * D;
-    return *(const uint4*)(vs + 8 * ld_c);
+  // Loader: thread t moves 16-byte chunk ld_c of the PASSES consecutive rows
+  // PASSES * ld_g + p of a tile.  A tile's rows all come from the cache or
+  // all from the window, so the base pointers are uniform and each load
+  // needs one offset; rows past a partial tile's end re-read its last row
+  // (in bounds; the score mask gives them zero weight).
+  const int ld_c = tid % CPR, ld_g = tid / CPR;
+  auto tile_base = [&](int t, const char*& kb, const char*& vb, int& nv) {
+    int lo;
+    tile_span(t, nct, P, k_end, lo, nv);
+    const bool in_cache = t < nct;
+    const size_t o = (size_t)(in_cache ? lo : lo - P) * D;
+    kb = (const char*)((in_cache ? kc : kw) + o);
+    vb = (const char*)((in_cache ? vc : vw) + o);
   };
   auto st = [&](int p, int buf, uint4 kx, uint4 vx) {
-    const int n = ld_n0 + RPP * p;
+    const int n = PASSES * ld_g + p;
     char* kt = smem + buf * 2 * TILE + n * RS + ((ld_c ^ swz(n)) << 4);
     *(uint4*)kt = kx;
     *(uint4*)(kt + TILE) = vx;
   };
   uint4 ak0, ak1, ak2, ak3, av0, av1, av2, av3;
   uint4 bk0, bk1, bk2, bk3, bv0, bv1, bv2, bv3;
-#define D2F_GLOAD(X, LO)                      \
-  {                                           \
-    X##k0 = ldk(0, LO); X##v0 = ldv(0, LO);   \
-    X##k1 = ldk(1, LO); X##v1 = ldv(1, LO);   \
-    if constexpr (PASSES > 2) {               \
-      X##k2 = ldk(2, LO); X##v2 = ldv(2, LO); \
-      X##k3 = ldk(3, LO); X##v3 = ldv(3, LO); \
-    }                                         \
+#define D2F_LD1(X, I)                                                       \
+  {                                                                         \
+    const int off_ = min(PASSES * ld_g + (I), nv_ - 1) * RS + 16 * ld_c;    \
+    X##k##I = *(const uint4*)(kb_ + off_);                                  \
+    X##v##I = *(const uint4*)(vb_ + off_);                                  \
+  }
+#define D2F_GLOAD(X, T)                    \
+  {                                        \
+    const char *kb_, *vb_;                 \
+    int nv_;                               \
+    tile_base((T), kb_, vb_, nv_);         \
+    D2F_LD1(X, 0)                          \
+    D2F_LD1(X, 1)                          \
+    if constexpr (PASSES > 2) {            \
+      D2F_LD1(X, 2)                        \
+      D2F_LD1(X, 3)                        \
+    }                                      \
   }
 #define D2F_LSTORE(X, BUF)      \
   {                             \
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     row_ok[qb] = row < rows;
     my_i[qb] = row_ok[qb] ? row / G : 0;
     my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
-    my_lim[qb] = min(k_hi, P + min(W, (my_i[qb] / B + 1) * B));
+    my_lim[qb] = P + min(W, (my_i[qb] / B + 1) * B);
     if (row_ok[qb]) {
       const __bf16* qp =
           (const __bf16*)a.q + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
@@ -177,9 +186,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
   const float c2 = a.c2;
 
-  auto compute = [&](int buf, int tile_lo) {
+  auto compute = [&](int buf, int t) {
     const char* Ks = smem + buf * 2 * TILE;
     const lds_char* Vs = (const lds_char*)(Ks + TILE);
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
     // S^T for this wave's 32 keys x 32 queries: [key block][query block].
     f32x4 sc[2][2];
 #pragma unroll
@@ -193,8 +204,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
         sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[1][s], sc[kb][1], 0, 0, 0);
       }
     }
-    const int key0 = tile_lo + 32 * kh + 4 * lg;  // key of sc[0][*][0]
-    const bool need_mask = tile_lo + kKTile > mask_from;
+    // Masking is needed on a partial tile and where a row's visible keys end.
+    const int kk0 = 32 * kh + 4 * lg;  // key within the tile of sc[0][*][0]
+    if (nv < kKTile || lo + kKTile > k_full) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int lim = min(nv, my_lim[qb] - lo);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kk0 + 16 * kb + r >= lim) sc[kb][qb][r] = kNegInf;
+      }
+    }
     bf16x8 pf[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -202,10 +224,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (need_mask && key0 + 16 * kb + r >= my_lim[qb]) sc[kb][qb][r] = kNegInf;
-          mx = fmaxf(mx, sc[kb][qb][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][qb][r]);
       }
       // Lazy rescaling: the reference max m_run only moves when some score
       // exceeds it by more than kSlack (base-2 units), so in the steady state
@@ -257,28 +276,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // count exactly which loads each wait covers; past the last tile they
   // re-read the last tile (cache hits) and fill a buffer nobody reads.
   if (n_tiles > 0) {
-    const int last_lo = k_lo + (n_tiles - 1) * kKTile;
-    auto tile_at = [&](int t) { return min(k_lo + t * kKTile, last_lo); };
+    auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
     D2F_GLOAD(a, tile_at(0));
     D2F_GLOAD(b, tile_at(1));
     D2F_LSTORE(a, 0);
     __syncthreads();
-    // Pairs of tiles; entering each pair, buffer 0 holds tile t and set b
-    // carries tile t+1.  One back-edge and one exit keep the compiler's
+    // Pairs of tiles; entering each pair, buffer 0 holds tile i and set b
+    // carries tile i+1.  One back-edge and one exit keep the compiler's
     // load-counter bookkeeping exact.
-    int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-      D2F_GLOAD(a, tile_at(t + 2));
-      if (wave_active) compute(0, k_lo + t * kKTile);
+    int i = 0;
+    for (; i + 1 < n_tiles; i += 2) {
+      D2F_GLOAD(a, tile_at(i + 2));
+      if (wave_active) compute(0, t_lo + i);
       D2F_LSTORE(b, 1);
       __syncthreads();
-      D2F_GLOAD(b, tile_at(t + 3));
-      if (wave_active) compute(1, k_lo + (t + 1) * kKTile);
+      D2F_GLOAD(b, tile_at(i + 3));
+      if (wave_active) compute(1, t_lo + i + 1);
       D2F_LSTORE(a, 0);
       __syncthreads();
     }
-    if (t < n_tiles && wave_active) compute(0, k_lo + t * kKTile);  // odd tail
+    if (i < n_tiles && wave_active) compute(0, t_lo + i);  // odd tail
   }
+#undef D2F_LD1
 #undef D2F_GLOAD
 #undef D2F_LSTORE
 

@@ -39,9 +39,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const int rows = G * W;
   const int r0 = qt * kQTile;
   const int k_end = tile_key_end(qt, P, W, G, B);
-  int k_lo, k_hi;
-  split_range(k_end, split, nsplit, k_lo, k_hi);
-  const int n_tiles = k_hi > k_lo ? (k_hi - k_lo + kKTile - 1) / kKTile : 0;
+  const int nct = cache_tiles(P);
+  int t_lo, t_hi;
+  split_tiles(nct + window_tiles(P, k_end), split, nsplit, t_lo, t_hi);
 
   const size_t head_c = ((size_t)rb * a.hkv + kvh) * (size_t)a.cap * D;
   const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const bool row_ok = my_row < rows;
   const int my_i = row_ok ? my_row / G : 0;
   const int my_h = kvh * G + (row_ok ? my_row % G : 0);
-  const int my_lim = min(k_hi, P + min(W, (my_i / B + 1) * B));
+  const int my_lim = P + min(W, (my_i / B + 1) * B);
 
   for (int e = tid; e < kQTile * D; e += kAttnThreads) {
     const int rr = e / D, d = e % D;
@@ -74,21 +74,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   for (int k = 0; k < D / 4; ++k) acc[k] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int tile_lo = k_lo + t * kKTile;
+  for (int t = t_lo; t < t_hi; ++t) {
+    int tile_lo, nv;
+    tile_span(t, nct, P, k_end, tile_lo, nv);
+    const bool in_cache = t < nct;
+    const float* ksrc = in_cache ? kc + (size_t)tile_lo * D : kw + (size_t)(tile_lo - P) * D;
+    const float* vsrc = in_cache ? vc + (size_t)tile_lo * D : vw + (size_t)(tile_lo - P) * D;
     __syncthreads();  // previous tile fully consumed (and Q tile stored)
     for (int e = tid; e < kKTile * D; e += kAttnThreads) {
-      const int n = e / D, d = e % D;
-      const int j = tile_lo + n;
-      float kv = 0.f, vv = 0.f;
-      if (j < k_hi) {
-        kv = (j < P) ? kc[(size_t)j * D + d] : kw[(size_t)(j - P) * D + d];
-        vv = (j < P) ? vc[(size_t)j * D + d] : vw[(size_t)(j - P) * D + d];
-      }
-      Ks[n][d] = kv;
-      Vs[n][d] = vv;
+      const int n = e / D;
+      const bool ok = n < nv;
+      Ks[n][e % D] = ok ? ksrc[e] : 0.f;
+      Vs[n][e % D] = ok ? vsrc[e] : 0.f;
     }
     __syncthreads();
+    const int lim = min(nv, my_lim - tile_lo);  // keys of this tile the row sees
 
     float x[16];
     float mx = kNegInf;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
 #pragma unroll 8
       for (int d = 0; d < D; ++d) s = fmaf(Qs[r][d], Ks[n][d], s);
       float v = s * a.c2;
-      if (tile_lo + n >= my_lim) v = kNegInf;
+      if (n >= lim) v = kNegInf;
       x[uu] = v;
       mx = fmaxf(mx, v);
     }

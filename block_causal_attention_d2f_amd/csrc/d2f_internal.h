@@ -73,12 +73,27 @@ __device__ __forceinline__ int tile_key_end(int qt, int P, int W, int G, int B) 
   return P + min(W, ((r_last / G) / B + 1) * B);
 }
 
-// Key range of split s of a query tile whose visible keys end at k_end: the
-// tile's ceil(k_end / kKTile) key tiles are divided as evenly as possible.
-__device__ __forceinline__ void split_range(int k_end, int s, int nsplit, int& k_lo, int& k_hi) {
-  const int nt = (k_end + kKTile - 1) / kKTile;
-  k_lo = (s * nt / nsplit) * kKTile;
-  k_hi = min(((s + 1) * nt / nsplit) * kKTile, k_end);
+// Key tiles of a query tile.  The cache [0, P) and the visible part of the
+// window [P, k_end) are tiled separately, so a tile never mixes cache and
+// window rows and has one base pointer per tensor; the last tile of each part
+// may be partial (nvalid < kKTile).
+__device__ __forceinline__ int cache_tiles(int P) { return (P + kKTile - 1) / kKTile; }
+__device__ __forceinline__ int window_tiles(int P, int k_end) {
+  return (k_end - P + kKTile - 1) / kKTile;
+}
+__device__ __forceinline__ void tile_span(int t, int nct, int P, int k_end, int& lo, int& nvalid) {
+  if (t < nct) {
+    lo = t * kKTile;
+    nvalid = min(kKTile, P - lo);
+  } else {
+    lo = P + (t - nct) * kKTile;
+    nvalid = min(kKTile, k_end - lo);
+  }
+}
+// Tiles [t_lo, t_hi) of split s: nt tiles divided as evenly as possible.
+__device__ __forceinline__ void split_tiles(int nt, int s, int nsplit, int& t_lo, int& t_hi) {
+  t_lo = s * nt / nsplit;
+  t_hi = (s + 1) * nt / nsplit;
 }
 
 // Workgroups are dealt round-robin over the 8 XCDs (workgroup x runs on XCD
