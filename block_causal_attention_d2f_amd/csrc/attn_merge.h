@@ -18,52 +18,46 @@ template <typename T> __device__ __forceinline__ T to_out(float x);
 template <> __device__ __forceinline__ float to_out<float>(float x) { return x; }
 template <> __device__ __forceinline__ __bf16 to_out<__bf16>(float x) { return (__bf16)x; }
 
-// 256 threads: four per row, each owning a contiguous quarter of head_dim.
+// Rows [row0, row0 + 1024 / D) of one group; D / 4 threads per row, each
+// owning 4 consecutive dims (one 16-byte load per split).  Loads of all
+// splits are independent, so a thread keeps many in flight.
 template <int D, typename OutT>
-__device__ void merge_group(const AttnArgs& a, int ri, int kvh, int qt) {
+__device__ void merge_rows(const AttnArgs& a, int ri, int kvh, int qt, int row0) {
   constexpr float kNegInf = -__builtin_inff();
   constexpr float kLn2 = 0.693147180559945309f;
-  constexpr int DQ = D / 4;
+  constexpr int TPR = D / 4;  // threads per row
   const int nsplit = a.req[ri].nsplit, qtiles = a.req[ri].qtiles;
   const int rb = a.req[ri].b, W = a.req[ri].win;
   const int G = a.group;
-  const int r = threadIdx.x >> 2, sub = threadIdx.x & 3;
+  const int r = row0 + (int)threadIdx.x / TPR, sub = (int)threadIdx.x % TPR;
   const int row = qt * kQTile + r;
-  if (row >= G * W) return;
+  if (r >= kQTile || row >= G * W) return;
   const int i = row / G, h = kvh * G + row % G;
   const size_t slot0 = ((size_t)(a.req[ri].unit_base + kvh * nsplit * qtiles + qt)) * kQTile + r;
   const size_t sstride = (size_t)qtiles * kQTile;  // slot distance between splits
 
   float m = kNegInf;
   for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.ws_ml[(slot0 + s * sstride) * 2]);
-  float acc[DQ];
-#pragma unroll
-  for (int k = 0; k < DQ; ++k) acc[k] = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float l = 0.f;
-  // Loads of the next split are independent of the current accumulation, so
-  // the compiler keeps several splits' reads in flight.
-#pragma unroll 2
+#pragma unroll 4
   for (int s = 0; s < nsplit; ++s) {
     const size_t sl = slot0 + s * sstride;
     const float2 ml = *(const float2*)(a.ws_ml + sl * 2);
+    const float4 v = *(const float4*)(a.ws_o + sl * D + 4 * sub);
     const float w = (ml.x == kNegInf) ? 0.f : exp2f(ml.x - m);
     l = fmaf(ml.y, w, l);
-    const float4* src = (const float4*)(a.ws_o + sl * D + sub * DQ);
-    float4 v[DQ / 4];
-#pragma unroll
-    for (int k = 0; k < DQ / 4; ++k) v[k] = src[k];
-#pragma unroll
-    for (int k = 0; k < DQ / 4; ++k) {
-      acc[4 * k + 0] = fmaf(v[k].x, w, acc[4 * k + 0]);
-      acc[4 * k + 1] = fmaf(v[k].y, w, acc[4 * k + 1]);
-      acc[4 * k + 2] = fmaf(v[k].z, w, acc[4 * k + 2]);
-      acc[4 * k + 3] = fmaf(v[k].w, w, acc[4 * k + 3]);
-    }
+    acc.x = fmaf(v.x, w, acc.x);
+    acc.y = fmaf(v.y, w, acc.y);
+    acc.z = fmaf(v.z, w, acc.z);
+    acc.w = fmaf(v.w, w, acc.w);
   }
   const float inv = 1.0f / l;
-  OutT* op = (OutT*)a.out + (((size_t)rb * a.hq + h) * a.wmax + i) * D + sub * DQ;
-#pragma unroll
-  for (int k = 0; k < DQ; ++k) op[k] = to_out<OutT>(acc[k] * inv);
+  OutT* op = (OutT*)a.out + (((size_t)rb * a.hq + h) * a.wmax + i) * D + 4 * sub;
+  op[0] = to_out<OutT>(acc.x * inv);
+  op[1] = to_out<OutT>(acc.y * inv);
+  op[2] = to_out<OutT>(acc.z * inv);
+  op[3] = to_out<OutT>(acc.w * inv);
   if (a.lse != nullptr && sub == 0)
     a.lse[((size_t)rb * a.hq + h) * a.wmax + i] = (m + log2f(l)) * kLn2;
 }

@@ -1,5 +1,6 @@
-// Split merge kernel: one workgroup per (request, KV head, query tile) of a
-// request whose key range was split; see attn_merge.h for the arithmetic.
+// Split merge kernel: 1024 / head_dim query rows of one (request, KV head,
+// query tile) group per workgroup, for requests whose key range was split;
+// see attn_merge.h for the arithmetic.
 #include "attn_merge.h"
 
 namespace d2f {
@@ -7,18 +8,21 @@ namespace {
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
-  const int g = blockIdx.x;
+  constexpr int RPW = 1024 / D;                // rows per workgroup
+  constexpr int SLICES = kQTile / RPW;         // workgroups per group
+  const int g = blockIdx.x / SLICES;
+  const int slice = blockIdx.x % SLICES;
   const int ri = find_req_group(a, g);
   if (a.req[ri].nsplit == 1) return;
   const int local = g - a.req[ri].group_base;
   const int qtiles = a.req[ri].qtiles;
-  merge_group<D, OutT>(a, ri, local / qtiles, local % qtiles);
+  merge_rows<D, OutT>(a, ri, local / qtiles, local % qtiles, slice * RPW);
 }
 
 }  // namespace
 
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, d2f_dtype_t dt, hipStream_t s) {
-  const dim3 grid(a.n_groups), block(256);
+  const dim3 grid(a.n_groups * (kQTile / (1024 / head_dim))), block(256);
   if (dt == D2F_BF16) {
     if (head_dim == 128) hipLaunchKernelGGL((attn_merge_kernel<128, __bf16>), grid, block, 0, s, a);
     else if (head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<64, __bf16>), grid, block, 0, s, a);
