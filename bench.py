@@ -80,7 +80,125 @@ def parse():
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE",
+                                                              "RUN_FETCH", "RUN_WRITE"),
+                    help="turn four rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of "
+                         "the copy calibration and of a bench run of --config) into "
+                         "profiles/traffic_<config>.txt; needs no GPU")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration(reps=5):
+    """A plain device-to-device copy of known size, the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms, _ = time_region(lambda: [dst.copy_(src) for _ in range(reps)])
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "reps": reps, "gbs": round(2 * COPY_BYTES * reps / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
+CALL_OF_KERNEL = (("attn_bf16_kernel", "d2f_block_attn"), ("attn_f32_kernel", "d2f_block_attn"),
+                  ("attn_merge_kernel", "d2f_block_attn"),
+                  ("vocab_reduce_kernel", "d2f_confidence_commit"),
+                  ("commit_decide_kernel", "d2f_confidence_commit"),
+                  ("kv_commit_kernel", "d2f_kv_commit"))
+
+
+def _counter_means(d, counter):
+    """Average per-dispatch value of `counter` for each kernel in a rocprofv3
+    --pmc csv output directory."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def summarize_counters(args):
+    cf = _counter_means(args.summarize_counters[0], "FETCH_SIZE")
+    cw = _counter_means(args.summarize_counters[1], "WRITE_SIZE")
+    rf = _counter_means(args.summarize_counters[2], "FETCH_SIZE")
+    rw = _counter_means(args.summarize_counters[3], "WRITE_SIZE")
+    copy_kernel = max(cf, key=cf.get)  # the 512 MiB copy dominates the calibration run
+    f_fetch = (COPY_BYTES / 1024) / cf[copy_kernel]
+    f_write = (COPY_BYTES / 1024) / cw[copy_kernel]
+    calls = {}
+    for name in rf:
+        call = next((c for k, c in CALL_OF_KERNEL if k in name), None)
+        if call is None:
+            continue
+        e = calls.setdefault(call, {"kernels": {}, "bytes_per_call": 0.0})
+        fb = rf[name] * 1024 * f_fetch
+        wb = rw.get(name, 0.0) * 1024 * f_write
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        short = short.replace("void ", "").replace("d2f::", "")
+        e["kernels"][short] = {"fetch_kib": round(rf[name], 1),
+                                                  "write_kib": round(rw.get(name, 0.0), 1),
+                                                  "bytes": round(fb + wb)}
+        e["bytes_per_call"] += fb + wb
+    rec = {"config": args.config, "source_hash": kernel_source_hash(),
+           "calibration": {"kernel": copy_kernel[:60], "copy_bytes": COPY_BYTES,
+                           "fetch_kib": round(cf[copy_kernel], 1),
+                           "write_kib": round(cw[copy_kernel], 1),
+                           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+           "calls": calls}
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.txt")
+    hdr = (f"HBM traffic per call for workload {args.config} from rocprofv3 counters.\n"
+           "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are averaged per kernel and scaled by\n"
+           "what the same counters read for a plain 512 MiB device copy (calibration).\n"
+           "Commands (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, each\n"
+           "counter in its own run):\n"
+           "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"
+           "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"
+           f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
+           f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
+           f"  python3 bench.py --config {args.config} --summarize-counters <4 dirs>\n"
+           "bench.py reports bytes_per_call as roofline.traffic only while source_hash matches.\n")
+    with open(path, "w") as f:
+        f.write(hdr + "\n---\n" + json.dumps(rec, indent=1) + "\n")
+    print(path)
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counter-derived traffic is only reported for
+    the build it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "block_causal_attention_d2f_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_name, call):
+    """HBM bytes per launch of `call` from the committed counter summary
+    (profiles/traffic_<config>.txt), or None when absent or measured on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config_name}.txt")
+    try:
+        rec = json.loads(open(path).read().split("\n---\n")[-1])
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    c = rec.get("calls", {}).get(call)
+    return None if c is None else c.get("bytes_per_call")
 
 
 class Workload:
@@ -280,14 +398,20 @@ def cpu_baseline(wl, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the D2F step here runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
     import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import block_causal_attention_d2f_amd as d2f
     d2f.load()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     K, Wu = args.steps, args.warmup
     n_masks = Wu + K + args.call_reps + 1
     wl = Workload(args.config, args.block_size, n_masks)
@@ -338,7 +462,7 @@ def main():
                     peak=PEAK_HBM_GBS, unit="GB/s")
         per_launch = kv_b
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.config, dom)
     roof["avg_us"] = round(shares[dom] / (wl.layers if dom == "d2f_block_attn" else 1) * 1e6, 3)
     roof["algorithmic_bytes_per_launch"] = per_launch
 
