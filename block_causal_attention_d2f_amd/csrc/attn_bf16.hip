@@ -9,9 +9,13 @@
 // and never loads a tile that lies wholly past a tile's last visible key.
 //
 // Design (one workgroup = 4 waves = one work unit, see d2f_internal.h):
-//  * K and V tiles of 64 keys are staged HBM -> registers -> LDS with 16-byte
-//    coalesced loads: two register sets and two LDS buffers keep the loads
-//    of the next two tiles in flight while the current one is consumed.
+//  * K and V tiles of 64 keys go HBM -> LDS with the gfx950 direct loads
+//    (global_load_lds_dwordx4: each lane's 16 bytes land in LDS without
+//    passing through registers).  Two LDS stages alternate: while the waves
+//    work on one tile, the next one streams into the other stage.  Each
+//    stage is a separate LDS variable and the tile loop is unrolled by two,
+//    so the compiler can tell the stage being read from the one being
+//    filled and never waits for the in-flight tile before an LDS read.
 //  * The LDS rows are unpadded and their 16-byte chunks XOR-swizzled by row,
 //    which makes both LDS read patterns below free of bank conflicts.
 //  * Wave w works on query rows [32 (w & 1), +32) -- two 16-row MFMA blocks --
@@ -32,6 +36,8 @@
 //  * A unit either covers all keys of its rows (writes O in bf16 and the LSE)
 //    or one key range (writes unnormalised O, running max and sum in fp32,
 //    merged exactly by attn_merge.hip).
+#include <type_traits>
+
 #include "d2f_internal.h"
 
 namespace d2f {
@@ -44,11 +50,13 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+template <int V> using ic = std::integral_constant<int, V>;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
-// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+// s_waitcnt immediates: vmcnt(0) alone, and vmcnt(0) with lgkmcnt(0).
 constexpr int kVmcntZero = 0x0F70;
+constexpr int kVmLgkmZero = 0x0070;
 // Largest excess (base-2 units) of a score over the running reference max
 // before the reference is raised: probabilities stay below 2^kSlack.
 constexpr float kSlack = 8.0f;
@@ -59,18 +67,50 @@ constexpr float kSlack = 8.0f;
 // {2d, 2d+1} land on 8 different bank groups (V transpose reads).
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
+// Direct 16-byte load HBM -> LDS (global_load_lds_dwordx4): lane l's bytes at
+// base + voff land at LDS address lds_addr + 16 l; base and lds_addr are
+// wave-uniform.  Issued as inline assembly so that the compiler, which cannot
+// tell which LDS stage such a load targets, does not hold every later LDS
+// read until all of them have landed; completion is awaited explicitly (the
+// load counter, then a barrier) before a stage is read.  M0 carries the LDS
+// address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void load_lds16(const void* base, int voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0"
+               :
+               : "s"(base), "v"(voff), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS stage J of the tile ring: [K tile][V tile], rows of 2D bytes.
+template <int J, int BYTES>
+__device__ __forceinline__ char* stage_buf() {
+  __shared__ __attribute__((aligned(16))) char buf[BYTES];
+  return buf;
+}
+
+// Workgroup barrier after this wave's own direct loads have landed and its
+// LDS reads have returned.  The waits are explicit, so the barrier carries no
+// fence of its own (a fence would also wait for the tile just issued); the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(kVmLgkmZero);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;                // LDS row bytes
   constexpr int KSTEPS = D / 32;           // MFMA k-steps over head_dim
   constexpr int DBLK = D / 16;             // 16-dim blocks of the output
   constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
-  constexpr int RPP = kAttnThreads / CPR;  // rows loaded per pass
-  constexpr int PASSES = kKTile / RPP;
   constexpr int TILE = kKTile * RS;        // bytes per K (or V) tile
-  static_assert(PASSES == 2 || PASSES == 4, "loader covers 2 or 4 passes");
-  static_assert(2 * (2 * DBLK * 64 * 4 + 2 * 64 * 2) * 4 <= 4 * TILE, "merge area fits");
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [buf][K,V][key][dim]
+  constexpr int RPB = 1024 / RS;           // rows per 1 KB direct-load block
+  constexpr int LPW = TILE / 1024 / 4;     // blocks per wave per tensor per tile
+  static_assert(LPW >= 1 && LPW * 4 * 1024 == TILE, "4 waves cover a tile in 1 KB blocks");
+  static_assert(2 * DBLK * 64 * 4 * 2 * 4 <= 2 * TILE && 2 * 64 * 2 * 2 * 4 <= 2 * TILE,
+                "merge area fits the two stages");
 
   const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
@@ -103,12 +143,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int lc = lane & 15, lg = lane >> 4;
   const int qh = wave & 1, kh = wave >> 1;
 
-  // Loader: thread t moves 16-byte chunk ld_c of the PASSES consecutive rows
-  // PASSES * ld_g + p of a tile.  A tile's rows all come from the cache or
-  // all from the window, so the base pointers are uniform and each load
-  // needs one offset; rows past a partial tile's end re-read its last row
-  // (in bounds; the score mask gives them zero weight).
-  const int ld_c = tid % CPR, ld_g = tid / CPR;
+  // Loader: tile rows are copied in 1 KB blocks, one direct load per wave
+  // and block; lane l of block j carries the 16 bytes that belong at LDS
+  // position (row RPB j + l / CPR, chunk l % CPR), i.e. global chunk
+  // (l % CPR) ^ swz(row) of that row.  A tile's rows all come from the cache
+  // or all from the window, so the base pointers are uniform.  Rows past a
+  // partial tile's end re-read its last row (in bounds; the score mask gives
+  // them zero weight).
   auto tile_base = [&](int t, const char*& kb, const char*& vb, int& nv) {
     int lo;
     tile_span(t, nct, P, k_end, lo, nv);
@@ -117,41 +158,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     kb = (const char*)((in_cache ? kc : kw) + o);
     vb = (const char*)((in_cache ? vc : vw) + o);
   };
-  auto st = [&](int p, int buf, uint4 kx, uint4 vx) {
-    const int n = PASSES * ld_g + p;
-    char* kt = smem + buf * 2 * TILE + n * RS + ((ld_c ^ swz(n)) << 4);
-    *(uint4*)kt = kx;
-    *(uint4*)(kt + TILE) = vx;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue = [&](auto J, int t) {
+    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, 2 * TILE>();
+    const char *kb, *vb;
+    int nv;
+    tile_base(t, kb, vb, nv);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = LPW * wave_u + j;
+      const int row = RPB * blk + lane / CPR;
+      const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz(row));
+      load_lds16(kb, off, sb + blk * 1024);
+      load_lds16(vb, off, sb + TILE + blk * 1024);
+    }
   };
-  uint4 ak0, ak1, ak2, ak3, av0, av1, av2, av3;
-  uint4 bk0, bk1, bk2, bk3, bv0, bv1, bv2, bv3;
-#define D2F_LD1(X, I)                                                       \
-  {                                                                         \
-    const int off_ = min(PASSES * ld_g + (I), nv_ - 1) * RS + 16 * ld_c;    \
-    X##k##I = *(const uint4*)(kb_ + off_);                                  \
-    X##v##I = *(const uint4*)(vb_ + off_);                                  \
-  }
-#define D2F_GLOAD(X, T)                    \
-  {                                        \
-    const char *kb_, *vb_;                 \
-    int nv_;                               \
-    tile_base((T), kb_, vb_, nv_);         \
-    D2F_LD1(X, 0)                          \
-    D2F_LD1(X, 1)                          \
-    if constexpr (PASSES > 2) {            \
-      D2F_LD1(X, 2)                        \
-      D2F_LD1(X, 3)                        \
-    }                                      \
-  }
-#define D2F_LSTORE(X, BUF)      \
-  {                             \
-    st(0, BUF, X##k0, X##v0);   \
-    st(1, BUF, X##k1, X##v1);   \
-    if constexpr (PASSES > 2) { \
-      st(2, BUF, X##k2, X##v2); \
-      st(3, BUF, X##k3, X##v3); \
-    }                           \
-  }
 
   // This lane's two queries (MFMA column lc of the wave's two row blocks).
   int my_i[2], my_h[2], my_lim[2];
@@ -186,8 +207,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
   const float c2 = a.c2;
 
-  auto compute = [&](int buf, int t) {
-    const char* Ks = smem + buf * 2 * TILE;
+  auto compute = [&](auto J, int t) {
+    const char* Ks = stage_buf<decltype(J)::value, 2 * TILE>();
     const lds_char* Vs = (const lds_char*)(Ks + TILE);
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
@@ -272,34 +293,29 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     }
   };
 
-  // Loads and LDS stores are issued unconditionally so that the compiler can
-  // count exactly which loads each wait covers; past the last tile they
-  // re-read the last tile (cache hits) and fill a buffer nobody reads.
+  // The tile after the last is issued too (re-reading the last tile, a cache
+  // hit) so that every wait covers exactly one tile; it is drained before the
+  // stages are reused below.
   if (n_tiles > 0) {
     auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
-    D2F_GLOAD(a, tile_at(0));
-    D2F_GLOAD(b, tile_at(1));
-    D2F_LSTORE(a, 0);
-    __syncthreads();
-    // Pairs of tiles; entering each pair, buffer 0 holds tile i and set b
-    // carries tile i+1.  One back-edge and one exit keep the compiler's
-    // load-counter bookkeeping exact.
+    issue(ic<0>{}, tile_at(0));
+    // Stage 0 holds tile i on entry to each pair.  The barrier at the top of
+    // a step both publishes the tile every wave loaded and retires the reads
+    // of the tile before it, whose stage the next load then refills.
     int i = 0;
-    for (; i + 1 < n_tiles; i += 2) {
-      D2F_GLOAD(a, tile_at(i + 2));
-      if (wave_active) compute(0, t_lo + i);
-      D2F_LSTORE(b, 1);
-      __syncthreads();
-      D2F_GLOAD(b, tile_at(i + 3));
-      if (wave_active) compute(1, t_lo + i + 1);
-      D2F_LSTORE(a, 0);
-      __syncthreads();
+    for (; i + 2 <= n_tiles; i += 2) {
+      tile_barrier();
+      issue(ic<1>{}, tile_at(i + 1));
+      if (wave_active) compute(ic<0>{}, t_lo + i);
+      tile_barrier();
+      issue(ic<0>{}, tile_at(i + 2));
+      if (wave_active) compute(ic<1>{}, t_lo + i + 1);
     }
-    if (i < n_tiles && wave_active) compute(0, t_lo + i);  // odd tail
+    if (i < n_tiles) {  // odd tail
+      tile_barrier();
+      if (wave_active) compute(ic<0>{}, t_lo + i);
+    }
   }
-#undef D2F_LD1
-#undef D2F_GLOAD
-#undef D2F_LSTORE
 
   // Per-lane partial sums to per-query sums (the 4 lanes of a query column).
 #pragma unroll
@@ -311,9 +327,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // Merge the two key halves: the wave of key half 1 hands (m, l, O) to the
   // wave of key half 0 with the same query half through LDS (same lane,
   // same register layout).
-  __syncthreads();  // tile buffers are free from here on
-  float* xo = (float*)smem + (size_t)qh * (2 * DBLK * 64 * 4);  // [qb][d][lane][4]
-  float* xml = (float*)smem + 2 * (2 * DBLK * 64 * 4) + qh * (2 * 64 * 2);
+  tile_barrier();  // no load in flight, no tile read pending: the stages are free
+  float* xo = (float*)stage_buf<0, 2 * TILE>() + (size_t)qh * (2 * DBLK * 64 * 4);  // [qb][d][lane][4]
+  float* xml = (float*)stage_buf<1, 2 * TILE>() + qh * (2 * 64 * 2);
   if (kh == 1 && wave_active) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
