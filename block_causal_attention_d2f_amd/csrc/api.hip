@@ -29,12 +29,20 @@ d2f_status_t hip_fail(hipError_t e, const char* what) {
   return fail(D2F_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Work-unit sizing.  The key tiles of all (request, KV head, query tile)
-// groups are cut into units of about C tiles, C = total tiles / (workgroups
-// resident on the device at once), so that one round of workgroups covers
-// the call: a second, mostly empty round would cost as much as the first.
-// Units never get shorter than kMinChunkTiles tiles.
+// Work-unit sizing.  The key tiles of a (request, KV head, query tile) group
+// may be cut into nsplit key ranges, one workgroup each, at the price of a
+// merge pass over fp32 partial results.  A split only pays when a request's
+// units would run much longer than the average load of a workgroup slot
+// (a long prefix among short ones, or too few groups to occupy the device).
+// With C = total key tiles / (kSlotFill x resident workgroups), a request is
+// split, into ceil(tiles / C) ranges, only if its longest query tile has more
+// than kSplitFactor x C tiles.  (Measured on MI355X, bf16 head_dim 128: with
+// 512 or more groups any split was slower; with 32 groups, 256 to 512 units
+// were within 3% of the best.)  Units never get shorter than kMinChunkTiles
+// tiles.
 constexpr int kMinChunkTiles = 2;
+constexpr double kSlotFill = 0.75;
+constexpr long long kSplitFactor = 2;
 constexpr int kDefaultCUs = 256;        // MI355X, used when no device is visible
 constexpr int kDefaultWgsPerCU = 2;
 
@@ -147,7 +155,8 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
       total_tiles += (long long)d->n_heads_kv *
                      host_key_tiles(prefix[b], host_tile_key_end(qt, prefix[b], W, G, B));
   }
-  const long long slots = resident_workgroups(d->dtype, d->head_dim);
+  const long long slots = std::max<long long>(
+      1, (long long)(kSlotFill * (double)resident_workgroups(d->dtype, d->head_dim)));
   const long long chunk_tiles =
       std::max<long long>(kMinChunkTiles, (total_tiles + slots - 1) / slots);
   size_t ws = 0;
@@ -165,7 +174,10 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
       // The last query tile sees the most keys; it sets the split count.
       const long long tiles =
           host_key_tiles(r.prefix, host_tile_key_end(r.qtiles - 1, r.prefix, r.win, G, B));
-      r.nsplit = (int)std::max<long long>(1, (tiles + chunk_tiles - 1) / chunk_tiles);
+      r.nsplit = 1;
+      if (tiles > kSplitFactor * chunk_tiles)
+        r.nsplit = (int)std::min<long long>(tiles / kMinChunkTiles,
+                                            (tiles + chunk_tiles - 1) / chunk_tiles);
       if (r.nsplit > 1) L.any_split = true;
       if (r.qtiles > 1) L.remap = true;
       reqs.push_back({(tiles + r.nsplit - 1) / r.nsplit, r});

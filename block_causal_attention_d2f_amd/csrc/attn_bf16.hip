@@ -212,17 +212,44 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     const lds_char* Vs = (const lds_char*)(Ks + TILE);
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
+    // All LDS reads of the tile are issued first -- K fragments, then the
+    // transposed V fragments -- so their latency is paid once and the V reads
+    // complete while the scores and probabilities are computed.  Lane (lc, lg)
+    // of a transposed read gets V[key 32kh + 4lg + e][dim 16d + lc] for e < 4
+    // (and +16 keys from the second read): k-slots 8lg..8lg+7 of the PV
+    // product, in the same key order as the lane's probabilities.
+    bf16x8 ka[2][KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int n = 32 * kh + 16 * kb + lc;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        ka[kb][s] = *(const bf16x8*)(Ks + n * RS + (((4 * s + lg) ^ swz(n)) << 4));
+    }
+    bf16x8 va[DBLK];
+    {
+      const int vr = 32 * kh + 4 * lg + (lc >> 2);
+      const int vbyte = (lc & 1) << 3;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) {
+        const int cidx = 2 * d + ((lc & 3) >> 1);
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz(vr)) << 4) + vbyte));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz(vr + 16)) << 4) + vbyte));
+        const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        va[d] = __builtin_bit_cast(bf16x8, both);
+      }
+    }
     // S^T for this wave's 32 keys x 32 queries: [key block][query block].
     f32x4 sc[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int n = 32 * kh + 16 * kb + lc;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + n * RS + (((4 * s + lg) ^ swz(n)) << 4));
-        sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[0][s], sc[kb][0], 0, 0, 0);
-        sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[1][s], sc[kb][1], 0, 0, 0);
+        sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qf[0][s], sc[kb][0], 0, 0, 0);
+        sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qf[1][s], sc[kb][1], 0, 0, 0);
       }
     }
     // Masking is needed on a partial tile and where a row's visible keys end.
@@ -273,23 +300,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
       }
       l_run[qb] += ps;  // this lane's keys only; lanes are summed once at the end
     }
-    // O^T += V^T P^T over this wave's 32 keys.  Lane (lc, lg) of the
-    // transposed read gets V[key 32kh + 4lg + e][dim 16d + lc] for e < 4
-    // (and +16 keys from the second read): k-slots 8lg..8lg+7 in the same
-    // key order as the lane's probabilities.
-    const int vr = 32 * kh + 4 * lg + (lc >> 2);
-    const int vbyte = (lc & 1) << 3;
+    // O^T += V^T P^T over this wave's 32 keys.
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
-      const int cidx = 2 * d + ((lc & 3) >> 1);
-      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz(vr)) << 4) + vbyte));
-      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz(vr + 16)) << 4) + vbyte));
-      const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-      const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-      o[d][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[0], o[d][0], 0, 0, 0);
-      o[d][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[1], o[d][1], 0, 0, 0);
+      o[d][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[0], o[d][0], 0, 0, 0);
+      o[d][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[1], o[d][1], 0, 0, 0);
     }
   };
 
