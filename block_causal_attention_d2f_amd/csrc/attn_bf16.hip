@@ -61,11 +61,21 @@ constexpr int kVmLgkmZero = 0x0070;
 // before the reference is raised: probabilities stay below 2^kSlack.
 constexpr float kSlack = 8.0f;
 
-// Swizzle of 16-byte chunk positions within an LDS row.  Rows 0..7 map one
-// chunk to 8 different bank groups (K fragment reads: 8 rows, same chunk),
-// and for 4 consecutive rows starting at a multiple of 4 the chunk pairs
-// {2d, 2d+1} land on 8 different bank groups (V transpose reads).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Swizzle of 16-byte chunk positions within an LDS row (chunk c of row n is
+// stored at position c ^ swz(n)).  The gfx950 LDS serves 256 bytes (64 banks)
+// per cycle; the swizzle makes both read patterns of the kernel conflict-free
+// -- the K fragment reads (ds_read_b128: 16 consecutive rows, one chunk each)
+// and the transposed V reads (ds_read_b64_tr_b16: 16 rows, two adjacent
+// chunks each) -- as measured with the SQ_LDS_BANK_CONFLICT counter on
+// MI355X.  For the transposed reads, each group of 8 rows must spread its
+// chunk pairs {2d, 2d+1} over 8 different pair positions.
+//   D = 128 (256-byte rows): n -> 2 (n mod 8), with bit 3 of n adding 9 (xor).
+//   D = 64 (128-byte rows, two per 256-byte bank line): n -> n & 6.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 7) << 1) ^ (((row >> 3) & 1) * 9);
+  else return row & 6;
+}
 
 // Direct 16-byte load HBM -> LDS (global_load_lds_dwordx4): lane l's bytes at
 // base + voff land at LDS address lds_addr + 16 l; base and lds_addr are
@@ -73,9 +83,10 @@ __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >>
 // tell which LDS stage such a load targets, does not hold every later LDS
 // read until all of them have landed; completion is awaited explicitly (the
 // load counter, then a barrier) before a stage is read.  M0 carries the LDS
-// address; nothing else in these kernels uses M0.
+// address (nothing else in these kernels uses M0); an LDS DMA must not read
+// M0 in the cycle after a scalar write to it, hence the s_nop.
 __device__ __forceinline__ void load_lds16(const void* base, int voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
                :
                : "s"(base), "v"(voff), "s"(lds_addr)
                : "memory", "m0");
@@ -168,11 +179,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     for (int j = 0; j < LPW; ++j) {
       const int blk = LPW * wave_u + j;
       const int row = RPB * blk + lane / CPR;
-      const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz(row));
+      const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
       load_lds16(kb, off, sb + blk * 1024);
       load_lds16(vb, off, sb + TILE + blk * 1024);
     }
   };
+
+  // The first tile is requested before the queries are loaded, so that its
+  // latency and theirs overlap.  Tiles past the last re-read the last tile.
+  auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
+  if (n_tiles > 0) issue(ic<0>{}, tile_at(0));
 
   // This lane's two queries (MFMA column lc of the wave's two row blocks).
   int my_i[2], my_h[2], my_lim[2];
@@ -196,9 +212,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     }
   }
   const bool wave_active = (r0 + 32 * qh) < rows;
-  // Retire the Q loads here: left pending, they would make the first use in
-  // the tile loop wait on the in-order load counter every iteration, i.e. on
-  // the prefetched tiles too.
+  // Retire the Q loads (and the first tile) here: left pending, they would
+  // make the first use in the tile loop wait on the in-order load counter
+  // every iteration, i.e. on the prefetched tiles too.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
 
   f32x4 o[DBLK][2];
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
       const int n = 32 * kh + 16 * kb + lc;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
-        ka[kb][s] = *(const bf16x8*)(Ks + n * RS + (((4 * s + lg) ^ swz(n)) << 4));
+        ka[kb][s] = *(const bf16x8*)(Ks + n * RS + (((4 * s + lg) ^ swz<D>(n)) << 4));
     }
     bf16x8 va[DBLK];
     {
@@ -234,9 +250,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
       for (int d = 0; d < DBLK; ++d) {
         const int cidx = 2 * d + ((lc & 3) >> 1);
         const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz(vr)) << 4) + vbyte));
+            (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz<D>(vr)) << 4) + vbyte));
         const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz(vr + 16)) << 4) + vbyte));
+            (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz<D>(vr + 16)) << 4) + vbyte));
         const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
         va[d] = __builtin_bit_cast(bf16x8, both);
       }
@@ -312,9 +328,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // hit) so that every wait covers exactly one tile; it is drained before the
   // stages are reused below.
   if (n_tiles > 0) {
-    auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
-    issue(ic<0>{}, tile_at(0));
-    // Stage 0 holds tile i on entry to each pair.  The barrier at the top of
+    // Stage 0 holds tile i on entry to each pair (tile 0 was requested
+    // before the query loads).  The barrier at the top of
     // a step both publishes the tile every wave loaded and retires the reads
     // of the tile before it, whose stage the next load then refills.
     int i = 0;

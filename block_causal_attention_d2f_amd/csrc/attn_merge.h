@@ -36,21 +36,45 @@ __device__ void merge_rows(const AttnArgs& a, int ri, int kvh, int qt, int row0)
   const size_t slot0 = ((size_t)(a.req[ri].unit_base + kvh * nsplit * qtiles + qt)) * kQTile + r;
   const size_t sstride = (size_t)qtiles * kQTile;  // slot distance between splits
 
-  float m = kNegInf;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.ws_ml[(slot0 + s * sstride) * 2]);
+  // Splits are taken kBatch at a time with all their loads in flight; a
+  // batch raises the running max and rescales what was accumulated before.
+  constexpr int kBatch = 16;
+  float m = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t sl = slot0 + s * sstride;
-    const float2 ml = *(const float2*)(a.ws_ml + sl * 2);
-    const float4 v = *(const float4*)(a.ws_o + sl * D + 4 * sub);
-    const float w = (ml.x == kNegInf) ? 0.f : exp2f(ml.x - m);
-    l = fmaf(ml.y, w, l);
-    acc.x = fmaf(v.x, w, acc.x);
-    acc.y = fmaf(v.y, w, acc.y);
-    acc.z = fmaf(v.z, w, acc.z);
-    acc.w = fmaf(v.w, w, acc.w);
+  for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+    float2 ml[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (s0 + k < nsplit) {
+        const size_t sl = slot0 + (size_t)(s0 + k) * sstride;
+        ml[k] = *(const float2*)(a.ws_ml + sl * 2);
+        v[k] = *(const float4*)(a.ws_o + sl * D + 4 * sub);
+      } else {
+        ml[k] = make_float2(kNegInf, 0.f);
+        v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, ml[k].x);
+    if (mb == kNegInf) continue;  // nothing visible so far
+    const float r = (m == kNegInf) ? 0.f : exp2f(m - mb);
+    l *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = (ml[k].x == kNegInf) ? 0.f : exp2f(ml[k].x - mb);
+      l = fmaf(ml[k].y, w, l);
+      acc.x = fmaf(v[k].x, w, acc.x);
+      acc.y = fmaf(v[k].y, w, acc.y);
+      acc.z = fmaf(v[k].z, w, acc.z);
+      acc.w = fmaf(v[k].w, w, acc.w);
+    }
+    m = mb;
   }
   const float inv = 1.0f / l;
   OutT* op = (OutT*)a.out + (((size_t)rb * a.hq + h) * a.wmax + i) * D + 4 * sub;
