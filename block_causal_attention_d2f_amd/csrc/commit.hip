@@ -15,13 +15,13 @@
 // cross-wave step), and the threads holding the maximum agree on its first
 // index.  COMMITTED rows are not read.
 //
-// Kernel 2 (commit_decide): one workgroup per D2F block.  The block's chunk
-// partials are staged through LDS 256 at a time (one load per thread, so a
-// block needs a handful of memory round trips), each row merges its partials
-// in chunk order, conf = 1 / sum (the max term is exp(0) = 1) is compared with
-// the threshold, the aggressive top-k ranks the block's masked rows (ties to
-// the lower position), and the new mask state, tokens and per-block counts
-// are written.  No floating-point atomics: results are deterministic.
+// Kernel 2 (commit_decide): one workgroup per D2F block.  A thread per row
+// merges the row's chunk partials (loads in flight together, folded in chunk
+// order), conf = 1 / sum (the max term is exp(0) = 1) is
+// compared with the threshold, the aggressive top-k ranks the block's masked
+// rows (ties to the lower position), and the new mask state, tokens and
+// per-block counts are written.  No floating-point atomics: results are
+// deterministic.
 #include <climits>
 
 #include "d2f_internal.h"
@@ -139,16 +139,39 @@ __device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& resul
   }
 }
 
-constexpr int kRowsPerThread = kMaxCommitBlock / kCommitThreads;  // 4
+// Combine the chunk partials of every row of one block into s_conf / s_idx:
+// one thread per row loads kBatch partials at a time, all in flight, and
+// folds them in chunk order (a fixed order: the result does not depend on
+// timing).  The loads do not wait for the mask state: a row that is not
+// MASKED has no partials written, and what is read for it is discarded.
+__device__ void combine_rows(const CommitArgs& a, size_t row0, int B, float* s_conf, int* s_idx) {
+  constexpr int kBatch = 16;
+  const int nck = a.n_chunks;
+  for (int p = threadIdx.x; p < B; p += kCommitThreads) {
+    const bool live = a.mask_state[row0 + p] == D2F_MASKED;
+    const float4* src = a.partial + (row0 + p) * nck;
+    float m = kNegInf, sm = 0.f;
+    int ix = INT_MAX;
+    for (int c0 = 0; c0 < nck; c0 += kBatch) {
+      float4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        v[k] = (c0 + k < nck) ? src[c0 + k] : make_float4(kNegInf, 0.f, __int_as_float(INT_MAX), 0.f);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) combine(m, sm, ix, v[k].x, v[k].y, __float_as_int(v[k].z));
+    }
+    s_conf[p] = live ? 1.0f / sm : 0.f;
+    s_idx[p] = live ? ix : -1;
+  }
+}
 
 __global__ __launch_bounds__(kCommitThreads) void commit_decide_kernel(const CommitArgs a) {
   __shared__ float s_conf[kMaxCommitBlock];
   __shared__ int s_idx[kMaxCommitBlock];
   __shared__ unsigned char s_live[kMaxCommitBlock];
-  __shared__ float4 s_stage[kCommitThreads];
   __shared__ int s_cnt, s_incomplete;
   const int blk = blockIdx.x;
-  const int B = a.block_size, nck = a.n_chunks;
+  const int B = a.block_size;
   const size_t row0 = (size_t)blk * B;
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -156,47 +179,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_decide_kernel(const Com
     s_incomplete = 0;
   }
   for (int p = tid; p < B; p += kCommitThreads) s_live[p] = a.mask_state[row0 + p] == D2F_MASKED;
-  // Running (max, sum, index) of rows tid, tid + 256, ... (chunk order).
-  float rm[kRowsPerThread], rs[kRowsPerThread];
-  int ri[kRowsPerThread];
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    rm[k] = kNegInf;
-    rs[k] = 0.f;
-    ri[k] = INT_MAX;
-  }
-  __syncthreads();
-  const int total = B * nck;  // partials of the block, row-major [row][chunk]
-  for (int base = 0; base < total; base += kCommitThreads) {
-    const int e = base + tid;
-    if (e < total && s_live[e / nck]) s_stage[tid] = a.partial[row0 * nck + e];
-    __syncthreads();
-    const int hi = min(total, base + kCommitThreads);
-#pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) {
-      const int p = tid + k * kCommitThreads;
-      if (p >= B || !s_live[p]) continue;
-      const int c_lo = max(base, p * nck), c_hi = min(hi, (p + 1) * nck);
-      for (int c = c_lo; c < c_hi; ++c) {
-        const float4 v = s_stage[c - base];
-        if (c == p * nck) {
-          rm[k] = v.x;
-          rs[k] = v.y;
-          ri[k] = __float_as_int(v.z);
-        } else {
-          combine(rm[k], rs[k], ri[k], v.x, v.y, __float_as_int(v.z));
-        }
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < kRowsPerThread; ++k) {
-    const int p = tid + k * kCommitThreads;
-    if (p >= B) continue;
-    s_conf[p] = s_live[p] ? 1.0f / rs[k] : 0.f;
-    s_idx[p] = s_live[p] ? ri[k] : -1;
-  }
+  combine_rows(a, row0, B, s_conf, s_idx);
   __syncthreads();
   const bool aggressive = a.block_phase[blk] == D2F_AGGRESSIVE && a.k_aggr > 0;
   int cnt = 0, incomplete = 0;
