@@ -150,23 +150,25 @@ def summarize_counters(args):
                                                   "write_kib": round(rw.get(name, 0.0), 1),
                                                   "bytes": round(fb + wb)}
         e["bytes_per_call"] += fb + wb
-    rec = {"config": args.config, "source_hash": kernel_source_hash(),
+    key = traffic_key(args)
+    rec = {"config": key, "source_hash": kernel_source_hash(),
            "calibration": {"kernel": copy_kernel[:60], "copy_bytes": COPY_BYTES,
                            "fetch_kib": round(cf[copy_kernel], 1),
                            "write_kib": round(cw[copy_kernel], 1),
                            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
            "calls": calls}
-    path = os.path.join(ROOT, "profiles", f"traffic_{args.config}.txt")
-    hdr = (f"HBM traffic per call for workload {args.config} from rocprofv3 counters.\n"
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.txt")
+    bs = "" if args.block_size is None else f" --block-size {args.block_size}"
+    hdr = (f"HBM traffic per call for workload {key} from rocprofv3 counters.\n"
            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are averaged per kernel and scaled by\n"
            "what the same counters read for a plain 512 MiB device copy (calibration).\n"
            "Commands (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, each\n"
            "counter in its own run):\n"
            "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"
            "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"
-           f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
-           f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
-           f"  python3 bench.py --config {args.config} --summarize-counters <4 dirs>\n"
+           f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
+           f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
+           f"  python3 bench.py --config {args.config}{bs} --summarize-counters <4 dirs>\n"
            "bench.py reports bytes_per_call as roofline.traffic only while source_hash matches.\n")
     with open(path, "w") as f:
         f.write(hdr + "\n---\n" + json.dumps(rec, indent=1) + "\n")
@@ -184,6 +186,12 @@ def kernel_source_hash():
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def traffic_key(args):
+    """Name of a workload's counter summary: the config, plus the block size
+    when one is chosen explicitly (the GQA config is measured per B)."""
+    return args.config if args.block_size is None else f"{args.config}_b{args.block_size}"
 
 
 def measured_traffic(config_name, call):
@@ -462,7 +470,7 @@ def main():
                     peak=PEAK_HBM_GBS, unit="GB/s")
         per_launch = kv_b
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(args.config, dom)
+    roof["traffic"] = measured_traffic(traffic_key(args), dom)
     roof["avg_us"] = round(shares[dom] / (wl.layers if dom == "d2f_block_attn" else 1) * 1e6, 3)
     roof["algorithmic_bytes_per_launch"] = per_launch
 

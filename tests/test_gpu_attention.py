@@ -58,6 +58,18 @@ def test_explicit_softmax_scale():
     compare_attn(shape, out, lse, ro, rl, label="scale0.3")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_many_groups_with_one_long_request(d):
+    # More (request, KV head) groups than CUs selects the two-stage ring; the
+    # long request is still cut into key ranges and merged.
+    nb = 20 if d == 128 else 40
+    hkv = 16 if d == 128 else 8
+    prefix = [6000] + [100 + 37 * i for i in range(nb - 1)]
+    shape = W.make_shape(nb, hkv, hkv, d, 16, prefix, [2] * nb, dtype="bf16")
+    pairs = [(0, h) for h in range(0, hkv, 3)] + [(b, b % hkv) for b in range(1, nb, 4)]
+    _check(shape, pairs=pairs, label=f"many-groups-d{d}")
+
+
 def test_cfg2_llada_single_step():
     c = W.config("cfg2")
     _check(c["shape"], label="cfg2")
