@@ -106,6 +106,19 @@ def test_block_sizes(bsz):
     compare_commit(ci, got, 0.8, 2, label=f"B{bsz}")
 
 
+def test_large_vocab_and_largest_block():
+    # vocab 300000: 37 chunk partials per row (the decide folds them in three
+    # batches); block 1024: four rows per decide thread.
+    ci = W.commit_inputs(32, 300000, 16, [W.AGGRESSIVE, W.CONSERVATIVE], 3.0, True,
+                         committed_frac=0.2, device="cuda", seed=300)
+    got = run_commit(ci, 0.8, 2)
+    compare_commit(ci, got, 0.8, 2, label="V300000")
+    ci = W.commit_inputs(2048, 700, 1024, [W.AGGRESSIVE, W.CONSERVATIVE], 1.5, True,
+                         committed_frac=0.3, device="cuda", seed=1024)
+    got = run_commit(ci, 0.5, 5)
+    compare_commit(ci, got, 0.5, 5, label="B1024")
+
+
 def test_hand_worked_fixture_on_gpu():
     rows, params, phases, blocks = [], {}, [], None
     for line in open(os.path.join(GOLDEN, "commit_worked_example.txt")):
