@@ -38,9 +38,9 @@ d2f_status_t hip_fail(hipError_t e, const char* what) {
 // split, into ceil(tiles / C) ranges, only if its longest query tile has more
 // than kSplitFactor x C tiles.  (Measured on MI355X, bf16 head_dim 128: with
 // 512 or more groups any split was slower; with 32 groups, 256 to 512 units
-// were within 3% of the best.)  Units never get shorter than kMinChunkTiles
-// tiles.
-constexpr int kMinChunkTiles = 2;
+// were within 3% of the best for a 32K prefix, and no split was best for a
+// 512-token prefix.)  Units never get shorter than kMinChunkTiles tiles.
+constexpr int kMinChunkTiles = 8;
 constexpr double kSlotFill = 0.75;
 constexpr long long kSplitFactor = 2;
 constexpr int kDefaultCUs = 256;        // MI355X, used when no device is visible
@@ -68,8 +68,9 @@ long long resident_workgroups(d2f_dtype_t dt, int head_dim) {
 }
 
 // Host copy of the kernel's visible-key end of query tile qt.
-long long host_tile_key_end(int qt, long long P, long long W, long long G, long long B) {
-  const long long r_last = std::min<long long>((qt + 1LL) * kQTile, G * W) - 1;
+long long host_tile_key_end(int qt, long long qrows, long long P, long long W, long long G,
+                            long long B) {
+  const long long r_last = std::min<long long>((qt + 1LL) * qrows, G * W) - 1;
   return P + std::min<long long>(W, ((r_last / G) / B + 1) * B);
 }
 
@@ -125,6 +126,7 @@ d2f_status_t check_lengths(const d2f_attn_desc_t* d, const int32_t* prefix, cons
 struct Launch {
   std::vector<ReqInfo> req;
   int n_units = 0, n_groups = 0;
+  int qrows = kQTile;  // query rows per unit
   bool any_split = false;
   bool remap = false;
 };
@@ -147,13 +149,19 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
                       std::vector<Launch>& out) {
   const int G = d->n_heads_q / d->n_heads_kv;
   const int B = d->block_size;
+  // Query rows per unit: when no request has more than 32 query rows per KV
+  // head, the bf16 kernel works on 32-row units (one 16-row block per wave),
+  // so that all four waves of a unit have rows instead of two.
+  long long max_rows = 0;
+  for (int b = 0; b < d->batch; ++b) max_rows = std::max<long long>(max_rows, (long long)G * nwin[b] * B);
+  const int qrows = (d->dtype == D2F_BF16 && max_rows <= 32) ? 32 : kQTile;
   long long total_tiles = 0;
   for (int b = 0; b < d->batch; ++b) {
     const long long W = (long long)nwin[b] * B;
-    const int qtiles = (int)((G * W + kQTile - 1) / kQTile);
+    const int qtiles = (int)((G * W + qrows - 1) / qrows);
     for (int qt = 0; qt < qtiles; ++qt)
       total_tiles += (long long)d->n_heads_kv *
-                     host_key_tiles(prefix[b], host_tile_key_end(qt, prefix[b], W, G, B));
+                     host_key_tiles(prefix[b], host_tile_key_end(qt, qrows, prefix[b], W, G, B));
   }
   const long long slots = std::max<long long>(
       1, (long long)(kSlotFill * (double)resident_workgroups(d->dtype, d->head_dim)));
@@ -163,6 +171,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
   out.clear();
   for (int b0 = 0; b0 < d->batch; b0 += kMaxReqPerLaunch) {
     Launch L;
+    L.qrows = qrows;
     const int b1 = std::min(d->batch, b0 + kMaxReqPerLaunch);
     std::vector<std::pair<long long, ReqInfo>> reqs;
     for (int b = b0; b < b1; ++b) {
@@ -170,10 +179,10 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
       r.b = b;
       r.prefix = prefix[b];
       r.win = nwin[b] * B;
-      r.qtiles = (G * r.win + kQTile - 1) / kQTile;
+      r.qtiles = (G * r.win + qrows - 1) / qrows;
       // The last query tile sees the most keys; it sets the split count.
-      const long long tiles =
-          host_key_tiles(r.prefix, host_tile_key_end(r.qtiles - 1, r.prefix, r.win, G, B));
+      const long long tiles = host_key_tiles(
+          r.prefix, host_tile_key_end(r.qtiles - 1, qrows, r.prefix, r.win, G, B));
       r.nsplit = 1;
       if (tiles > kSplitFactor * chunk_tiles)
         r.nsplit = (int)std::min<long long>(tiles / kMinChunkTiles,
@@ -293,6 +302,7 @@ d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const vo
     a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * kQTile * desc->head_dim
                           : nullptr;
     a.cap = desc->cache_capacity;
+    a.qrows = L.qrows;
     a.hq = desc->n_heads_q;
     a.hkv = desc->n_heads_kv;
     a.group = desc->n_heads_q / desc->n_heads_kv;

@@ -110,7 +110,8 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D>
+// QB: 16-row query blocks per wave (2: 64 query rows per unit, 1: 32).
+template <int D, int QB>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;                // LDS row bytes
   constexpr int KSTEPS = D / 32;           // MFMA k-steps over head_dim
@@ -134,8 +135,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int kvh = local / nsplit;
   const int G = a.group, B = a.bsz;
   const int rows = G * W;
-  const int r0 = qt * kQTile;
-  const int k_end = tile_key_end(qt, P, W, G, B);          // last key any row sees
+  constexpr int QROWS = 32 * QB;  // query rows of the unit
+  const int r0 = qt * QROWS;
+  const int k_end = tile_key_end(qt, QROWS, P, W, G, B);  // last key any row sees
   const int k_full = P + min(W, ((r0 / G) / B + 1) * B);  // keys every row sees
   const int nct = cache_tiles(P);
   int t_lo, t_hi;
@@ -191,12 +193,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   if (n_tiles > 0) issue(ic<0>{}, tile_at(0));
 
   // This lane's two queries (MFMA column lc of the wave's two row blocks).
-  int my_i[2], my_h[2], my_lim[2];
-  bool row_ok[2];
-  bf16x8 qf[2][KSTEPS];
+  int my_i[QB], my_h[QB], my_lim[QB];
+  bool row_ok[QB];
+  bf16x8 qf[QB][KSTEPS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = r0 + 32 * qh + 16 * qb + lc;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = r0 + 16 * QB * qh + 16 * qb + lc;
     row_ok[qb] = row < rows;
     my_i[qb] = row_ok[qb] ? row / G : 0;
     my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
@@ -211,16 +213,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
       for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = bf16x8{};
     }
   }
-  const bool wave_active = (r0 + 32 * qh) < rows;
+  const bool wave_active = (r0 + 16 * QB * qh) < rows;
   // Retire the Q loads (and the first tile) here: left pending, they would
   // make the first use in the tile loop wait on the in-order load counter
   // every iteration, i.e. on the prefetched tiles too.
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
 
-  f32x4 o[DBLK][2];
+  f32x4 o[DBLK][QB];
 #pragma unroll
-  for (int d = 0; d < DBLK; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+  for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[d][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_run[qb] = kNegInf, l_run[qb] = 0.f;
   const float c2 = a.c2;
 
   auto compute = [&](auto J, int t) {
@@ -257,22 +263,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
         va[d] = __builtin_bit_cast(bf16x8, both);
       }
     }
-    // S^T for this wave's 32 keys x 32 queries: [key block][query block].
-    f32x4 sc[2][2];
+    // S^T for this wave's 32 keys x 16 QB queries: [key block][query block].
+    f32x4 sc[2][QB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sc[kb][0] = sc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        sc[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qf[0][s], sc[kb][0], 0, 0, 0);
-        sc[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qf[1][s], sc[kb][1], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qf[qb][s], sc[kb][qb], 0, 0, 0);
       }
     }
     // Masking is needed on a partial tile and where a row's visible keys end.
     const int kk0 = 32 * kh + 4 * lg;  // key within the tile of sc[0][*][0]
     if (nv < kKTile || lo + kKTile > k_full) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const int lim = min(nv, my_lim[qb] - lo);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -281,9 +289,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
             if (kk0 + 16 * kb + r >= lim) sc[kb][qb][r] = kNegInf;
       }
     }
-    bf16x8 pf[2];
+    bf16x8 pf[QB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -319,8 +327,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     // O^T += V^T P^T over this wave's 32 keys.
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) {
-      o[d][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[0], o[d][0], 0, 0, 0);
-      o[d][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[1], o[d][1], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[d][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[qb], o[d][qb], 0, 0, 0);
     }
   };
 
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
 
   // Per-lane partial sums to per-query sums (the 4 lanes of a query column).
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     l_run[qb] += __shfl_xor(l_run[qb], 16);
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
@@ -358,11 +367,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // wave of key half 0 with the same query half through LDS (same lane,
   // same register layout).
   tile_barrier();  // no load in flight, no tile read pending: the stages are free
-  float* xo = (float*)stage_buf<0, 2 * TILE>() + (size_t)qh * (2 * DBLK * 64 * 4);  // [qb][d][lane][4]
-  float* xml = (float*)stage_buf<1, 2 * TILE>() + qh * (2 * 64 * 2);
+  float* xo = (float*)stage_buf<0, 2 * TILE>() + (size_t)qh * (QB * DBLK * 64 * 4);  // [qb][d][lane][4]
+  float* xml = (float*)stage_buf<1, 2 * TILE>() + qh * (QB * 64 * 2);
   if (kh == 1 && wave_active) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) = o[d][qb];
       xml[(qb * 64 + lane) * 2 + 0] = m_run[qb];
@@ -372,7 +381,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   __syncthreads();
   if (kh == 1 || !wave_active) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float m1 = xml[(qb * 64 + lane) * 2 + 0], l1 = xml[(qb * 64 + lane) * 2 + 1];
     const float m = fmaxf(m_run[qb], m1);
     const float w0 = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     if (!row_ok[qb]) continue;
     if (nsplit == 1) {
       const float inv = 1.0f / l_run[qb];
@@ -402,7 +411,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
         a.lse[((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]] =
             (m_run[qb] + log2f(l_run[qb])) * kLn2;
     } else {
-      const size_t row_slot = (size_t)u * kQTile + 32 * qh + 16 * qb + lc;
+      const size_t row_slot = (size_t)u * kQTile + 16 * QB * qh + 16 * qb + lc;
       float* wp = a.ws_o + row_slot * D;
 #pragma unroll
       for (int d = 0; d < DBLK; ++d) *(f32x4*)(wp + 16 * d + 4 * lg) = o[d][qb];
@@ -420,18 +429,23 @@ int attn_bf16_wgs_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128>, kAttnThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2>, kAttnThreads, 0);
   else if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64>, kAttnThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2>, kAttnThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.n_units), block(kAttnThreads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, s, a);
+  const bool narrow = a.qrows == 32;
+  if (head_dim == 128 && !narrow)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, block, 0, s, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, s, a);
+  else if (head_dim == 64 && !narrow)
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), grid, block, 0, s, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

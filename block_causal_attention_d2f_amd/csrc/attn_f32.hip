@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const int G = a.group, B = a.bsz;
   const int rows = G * W;
   const int r0 = qt * kQTile;
-  const int k_end = tile_key_end(qt, P, W, G, B);
+  const int k_end = tile_key_end(qt, kQTile, P, W, G, B);
   const int nct = cache_tiles(P);
   int t_lo, t_hi;
   split_tiles(nct + window_tiles(P, k_end), split, nsplit, t_lo, t_hi);

@@ -30,8 +30,8 @@ __device__ void merge_rows(const AttnArgs& a, int ri, int kvh, int qt, int row0)
   const int rb = a.req[ri].b, W = a.req[ri].win;
   const int G = a.group;
   const int r = row0 + (int)threadIdx.x / TPR, sub = (int)threadIdx.x % TPR;
-  const int row = qt * kQTile + r;
-  if (r >= kQTile || row >= G * W) return;
+  const int row = qt * a.qrows + r;
+  if (r >= a.qrows || row >= G * W) return;
   const int i = row / G, h = kvh * G + row % G;
   const size_t slot0 = ((size_t)(a.req[ri].unit_base + kvh * nsplit * qtiles + qt)) * kQTile + r;
   const size_t sstride = (size_t)qtiles * kQTile;  // slot distance between splits

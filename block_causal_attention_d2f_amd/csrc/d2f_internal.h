@@ -23,7 +23,7 @@ struct ReqInfo {
   int32_t b;          // batch index of the request
   int32_t prefix;     // P: cached tokens
   int32_t win;        // W: window tokens (n_win_blocks * block_size)
-  int32_t qtiles;     // ceil(group * W / kQTile)
+  int32_t qtiles;     // ceil(group * W / qrows)
   int32_t nsplit;     // key-range splits per query tile (1 = final outputs)
   int32_t unit_base;  // first work unit of this request within the launch
   int32_t group_base; // first (kv_head, qtile) merge group within the launch
@@ -44,6 +44,7 @@ struct AttnArgs {
   int32_t hq, hkv, group, wmax, bsz;
   int32_t n_req, n_units, n_groups;
   int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
+  int32_t qrows;  // query rows per unit: kQTile, or 32 (bf16, narrow windows)
   float c2;       // softmax scale * log2(e)
   ReqInfo req[kMaxReqPerLaunch];
 };
@@ -67,9 +68,10 @@ __device__ __forceinline__ int find_req_group(const AttnArgs& a, int g) {
   return lo;
 }
 
-// Visible-key end of query tile qt: the last row's window block bounds it.
-__device__ __forceinline__ int tile_key_end(int qt, int P, int W, int G, int B) {
-  const int r_last = min((qt + 1) * kQTile, G * W) - 1;
+// Visible-key end of query tile qt (qrows rows per tile): the last row's
+// window block bounds it.
+__device__ __forceinline__ int tile_key_end(int qt, int qrows, int P, int W, int G, int B) {
+  const int r_last = min((qt + 1) * qrows, G * W) - 1;
   return P + min(W, ((r_last / G) / B + 1) * B);
 }
 

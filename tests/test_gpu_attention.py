@@ -46,7 +46,7 @@ def test_edge_shapes(dtype, case):
 
 
 def test_fp32_head_dim_32_long_prefix():
-    shape = W.make_shape(2, 2, 2, 32, 16, [700, 33], [3, 2], dtype="f32")
+    shape = W.make_shape(2, 2, 2, 32, 16, [2100, 33], [3, 2], dtype="f32")
     _check(shape, label="f32-d32-split")
 
 

@@ -30,6 +30,17 @@ def test_graph_replays_match_eager():
     conf = torch.empty(rows, dtype=torch.float32, device="cuda")
     am = torch.empty(rows, dtype=torch.int32, device="cuda")
     kc, vc = x["k_cache"].clone(), x["v_cache"].clone()
+    # A second attention call with a long prefix: its keys are split across
+    # workgroups and merged by a second kernel inside the graph.
+    sh2 = W.make_shape(1, 8, 8, 128, 16, [8192], [2], dtype="bf16")
+    x2 = W.attn_inputs(sh2, device="cuda", seed=5)
+    out2 = torch.empty_like(x2["q"])
+    lse2 = torch.empty(x2["q"].shape[:3], dtype=torch.float32, device="cuda")
+    desc2 = d2f.make_desc(sh2.batch, sh2.n_heads_q, sh2.n_heads_kv, sh2.head_dim, sh2.block_size,
+                          sh2.max_win_blocks, sh2.cache_capacity, x2["q"].dtype)
+    need2 = d2f.d2f_block_attn_workspace_size(desc2, sh2.prefix_len, sh2.n_win_blocks)
+    assert need2 > 0
+    ws_a2 = torch.empty(need2, dtype=torch.uint8, device="cuda")
 
     def step():
         d2f.d2f_block_attn(x["q"], kc, vc, x["k_win"], x["v_win"], sh.prefix_len,
@@ -38,14 +49,17 @@ def test_graph_replays_match_eager():
                                   ci.mask_token_id, conf_out=conf, argmax_out=am, n_committed=nc,
                                   block_complete=bc, workspace=ws_c)
         d2f.d2f_kv_commit(kc, vc, x["k_win"], x["v_win"], list(sh.prefix_len), 0, sh.block_size)
+        d2f.d2f_block_attn(x2["q"], x2["k_cache"], x2["v_cache"], x2["k_win"], x2["v_win"],
+                           sh2.prefix_len, sh2.n_win_blocks, sh2.block_size, out=out2, lse=lse2,
+                           workspace=ws_a2)
 
     def snapshot():
-        return [t.clone() for t in (out, lse, ms, tok, nc, bc, conf, am, kc, vc)]
+        return [t.clone() for t in (out, lse, ms, tok, nc, bc, conf, am, kc, vc, out2, lse2)]
 
     def reset():
         ms.copy_(ci.mask_state)
         tok.copy_(ci.tokens)
-        for t in (out, lse, conf):
+        for t in (out, lse, conf, out2, lse2):
             t.fill_(0.0)
 
     reset()
