@@ -19,10 +19,11 @@ Modules:
   attention  block-causal window attention over a frozen cache
   commit     per-position confidence/argmax and the block commit rule
   kv_cache   appending a completed block to the cache
+  window     the active-window schedule of pipelined decoding
 
 Every function here is pinned by a CPU test against something other than
 itself (closed forms, library routines on special cases, invariants, brute
 force, hand-worked fixtures); see ``tests/test_oracle_*.py``.
 """
-from . import attention, commit, kv_cache  # noqa: F401
+from . import attention, commit, kv_cache, window  # noqa: F401
 from .common import as_f64  # noqa: F401
