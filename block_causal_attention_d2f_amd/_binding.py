@@ -27,7 +27,9 @@ CONSERVATIVE, AGGRESSIVE = 0, 1
 
 EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
+           "d2f_window_init", "d2f_window_after_commit",
            "d2f_status_string", "d2f_last_error", "d2f_version")
+MAX_WINDOW = 64  # D2F_MAX_WINDOW
 
 
 class D2FError(RuntimeError):
@@ -42,6 +44,19 @@ class AttnDesc(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("max_win_blocks", ctypes.c_int32),
                 ("cache_capacity", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float)]
+
+
+class WindowParams(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("max_win_blocks", ctypes.c_int32),
+                ("total_blocks", ctypes.c_int32), ("tau_add", ctypes.c_float),
+                ("tau_act", ctypes.c_float)]
+
+
+class WindowState(ctypes.Structure):
+    _fields_ = [("first", ctypes.c_int32), ("n_win", ctypes.c_int32),
+                ("started", ctypes.c_int32), ("persisted", ctypes.c_int32),
+                ("committed", ctypes.c_int32 * MAX_WINDOW),
+                ("phase", ctypes.c_uint8 * MAX_WINDOW)]
 
 
 _lib = None
@@ -70,6 +85,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "d2f_confidence_commit_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "d2f_confidence_commit": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                                          _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "d2f_window_init": (_i32, [ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState)]),
+        "d2f_window_after_commit": (_i32, [ctypes.POINTER(WindowParams),
+                                           ctypes.POINTER(WindowState), _pi32, _pi32, _pi32]),
         "d2f_status_string": (ctypes.c_char_p, [_i32]),
         "d2f_last_error": (ctypes.c_char_p, []),
         "d2f_version": (_i32, []),
@@ -231,3 +249,50 @@ def version() -> int:
 
 def softmax_scale_default(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+class Window:
+    """The library's active-window scheduler (host only; see d2f.h)."""
+
+    def __init__(self, block_size: int, max_win_blocks: int, total_blocks: int,
+                 tau_add: float, tau_act: float):
+        self.params = WindowParams(int(block_size), int(max_win_blocks), int(total_blocks),
+                                   float(tau_add), float(tau_act))
+        self.state = WindowState()
+        _check(load().d2f_window_init(ctypes.byref(self.params), ctypes.byref(self.state)))
+
+    @property
+    def first(self) -> int:
+        return self.state.first
+
+    @property
+    def n_win(self) -> int:
+        return self.state.n_win
+
+    @property
+    def started(self) -> int:
+        return self.state.started
+
+    @property
+    def persisted(self) -> int:
+        return self.state.persisted
+
+    @property
+    def done(self) -> bool:
+        return self.state.persisted == self.params.total_blocks
+
+    @property
+    def committed(self) -> list:
+        return [self.state.committed[k] for k in range(self.state.n_win)]
+
+    @property
+    def phase(self) -> list:
+        return [self.state.phase[k] for k in range(self.state.n_win)]
+
+    def after_commit(self, n_committed: Sequence[int]):
+        """Apply one commit pass; returns (blocks persisted, blocks appended)."""
+        p, a = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(load().d2f_window_after_commit(ctypes.byref(self.params), ctypes.byref(self.state),
+                                              _i32_array(n_committed), ctypes.byref(p),
+                                              ctypes.byref(a)))
+        return p.value, a.value

@@ -11,7 +11,6 @@
 #include "d2f_internal.h"
 
 namespace d2f {
-namespace {
 
 thread_local std::string g_last_error;
 
@@ -24,6 +23,8 @@ d2f_status_t fail(d2f_status_t st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+
+namespace {
 
 d2f_status_t hip_fail(hipError_t e, const char* what) {
   return fail(D2F_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

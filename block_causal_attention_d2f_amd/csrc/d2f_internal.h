@@ -134,6 +134,10 @@ constexpr int kCommitChunk = 8192;     // logits per workgroup (32 KiB)
 constexpr int kMaxCommitBlock = 1024;  // rows per D2F block handled by one workgroup
 hipError_t launch_confidence_commit(const CommitArgs& a, bool vec4, hipStream_t s);
 
+// Record a printf-style message as the calling thread's last error (read by
+// d2f_last_error) and return st.
+d2f_status_t fail(d2f_status_t st, const char* fmt, ...);
+
 struct KvArgs {
   void* kc;
   void* vc;

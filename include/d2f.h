@@ -201,6 +201,62 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
                                    uint8_t* block_complete, void* workspace,
                                    size_t workspace_bytes, d2f_stream_t stream);
 
+/* ---- Active-window schedule (host only; no device memory, no stream) ----
+ *
+ * [D2F-review] sections "핵심 메시지" (last point) and "쉽게 이해하기"
+ * (inference paragraph): decoding keeps a window of active blocks; once the
+ * progress of the last block passes a threshold a new, fully masked block is
+ * added behind it; a new block starts conservative and turns aggressive once
+ * the block before it has progressed far enough.  [D2F-wiki] section "운영
+ * 관점" (KV cache management): a completed block is persisted to the cache.
+ *
+ * Rules of this implementation (the pages give no numbers or tie rules):
+ * progress = committed positions / block_size; a threshold is passed when
+ * committed > tau * block_size (strict, in double precision of the float tau).
+ * After each commit pass (d2f_window_after_commit):
+ *   1. n_committed[k] (positions committed by the pass in window block k) is
+ *      added to the block's count;
+ *   2. while the oldest window block is complete it is persisted (the caller
+ *      then calls d2f_kv_commit for it, oldest first) and leaves the window;
+ *   3. if fewer than total_blocks blocks were started and the window holds
+ *      fewer than max_win_blocks blocks, one new block is appended when the
+ *      window is empty or its last block's progress passes tau_add;
+ *   4. phases for the next pass: the oldest block is AGGRESSIVE; block k > 0
+ *      becomes AGGRESSIVE when block k - 1's progress passes tau_act; a block
+ *      never returns to CONSERVATIVE.
+ * d2f_window_init starts the first block (AGGRESSIVE: it is the oldest).
+ * The state is a plain struct owned by the caller; window block k is absolute
+ * block first + k.  Errors: D2F_ERR_INVALID_ARG (block_size < 1, max_win_blocks
+ * outside 1..D2F_MAX_WINDOW, total_blocks < 1, NaN thresholds, a count that
+ * would exceed block_size or is negative, a call after every block was
+ * persisted).  On error the state is left unchanged. */
+#define D2F_MAX_WINDOW 64
+
+typedef struct {
+  int32_t block_size;      /* positions per block */
+  int32_t max_win_blocks;  /* most blocks in the window at once (1..D2F_MAX_WINDOW) */
+  int32_t total_blocks;    /* blocks to decode */
+  float tau_add;           /* append a block once the last one's progress passes this */
+  float tau_act;           /* a block turns aggressive once its predecessor passes this */
+} d2f_window_params_t;
+
+typedef struct {
+  int32_t first;       /* absolute index of the oldest window block */
+  int32_t n_win;       /* blocks in the window */
+  int32_t started;     /* blocks started so far */
+  int32_t persisted;   /* blocks persisted so far (== total_blocks when done) */
+  int32_t committed[D2F_MAX_WINDOW];  /* committed positions per window block */
+  uint8_t phase[D2F_MAX_WINDOW];      /* D2F_CONSERVATIVE / D2F_AGGRESSIVE per window block */
+} d2f_window_t;
+
+d2f_status_t d2f_window_init(const d2f_window_params_t* params, d2f_window_t* state);
+
+/* Apply one commit pass; *persisted_out = blocks persisted by step 2 (the
+ * caller appends their K/V oldest first), *appended_out = 0 or 1. */
+d2f_status_t d2f_window_after_commit(const d2f_window_params_t* params, d2f_window_t* state,
+                                     const int32_t* n_committed, int32_t* persisted_out,
+                                     int32_t* appended_out);
+
 /* Static text for a status code. */
 const char* d2f_status_string(d2f_status_t status);
 
