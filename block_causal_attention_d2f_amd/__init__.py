@@ -6,9 +6,11 @@ thin ctypes binding.
     d2f_confidence_commit   max-probability confidence + commit/remask
     d2f_kv_commit           append a completed block to the KV cache
     Window                  the active-window schedule (host)
+    d2f_decode_advance      one step's bookkeeping after the commit pass
 """
 from ._binding import (AGGRESSIVE, COMMITTED, CONSERVATIVE, D2F_BF16, D2F_F32, EXPORTS,  # noqa: F401
                        LIB_PATH, MASKED, AttnDesc, D2FError, Window, d2f_block_attn,
                        d2f_block_attn_workspace_size, d2f_confidence_commit,
-                       d2f_confidence_commit_workspace_size, d2f_kv_commit, load, make_desc,
+                       d2f_confidence_commit_workspace_size, d2f_decode_advance,
+                       d2f_kv_commit, load, make_desc,
                        version)

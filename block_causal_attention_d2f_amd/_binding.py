@@ -27,7 +27,7 @@ CONSERVATIVE, AGGRESSIVE = 0, 1
 
 EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
-           "d2f_window_init", "d2f_window_after_commit",
+           "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
            "d2f_status_string", "d2f_last_error", "d2f_version")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
 
@@ -88,6 +88,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "d2f_window_init": (_i32, [ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState)]),
         "d2f_window_after_commit": (_i32, [ctypes.POINTER(WindowParams),
                                            ctypes.POINTER(WindowState), _pi32, _pi32, _pi32]),
+        "d2f_decode_advance": (_i32, [pdesc, _i32, _vp, _vp, _i64, _vp, _vp, _i64,
+                                      ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState),
+                                      _pi32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _pi32, _pi32,
+                                      _vp]),
         "d2f_status_string": (ctypes.c_char_p, [_i32]),
         "d2f_last_error": (ctypes.c_char_p, []),
         "d2f_version": (_i32, []),
@@ -296,3 +300,63 @@ class Window:
                                               _i32_array(n_committed), ctypes.byref(p),
                                               ctypes.byref(a)))
         return p.value, a.value
+
+
+def d2f_decode_advance(k_cache, v_cache, k_win, v_win, windows: Sequence[Window],
+                       prefix_len: list, n_committed, mask_state, tokens, block_phase,
+                       out_tokens, mask_token_id: int, prefix_len_dev=None, stream=None):
+    """The step's bookkeeping after the commit pass (see d2f.h): schedule every
+    request's window, append persisted blocks' K/V, slide the slot rows.
+
+    Caches / windows as for d2f_kv_commit (one layer or a [L] stack);
+    mask_state uint8 / tokens int32 [batch * Wmax]; block_phase uint8 and
+    n_committed int32 [batch * max_win_blocks]; out_tokens int32
+    [batch][total_blocks * block_size].  `windows` (one Window per request,
+    same parameters) and `prefix_len` are updated in place.  Returns
+    (persisted, appended) per request."""
+    layered = k_cache.dim() == 5
+    kc0 = k_cache[0] if layered else k_cache
+    kw0 = k_win[0] if layered else k_win
+    n_layers = k_cache.shape[0] if layered else 1
+    nb, hkv, cap, d = kc0.shape
+    if len(windows) != nb or len(prefix_len) != nb:
+        raise ValueError("one window and one prefix length per request")
+    params = windows[0].params if nb else None
+    for w in windows:
+        if (w.params.block_size, w.params.max_win_blocks, w.params.total_blocks,
+                w.params.tau_add, w.params.tau_act) != \
+                (params.block_size, params.max_win_blocks, params.total_blocks, params.tau_add,
+                 params.tau_act):
+            raise ValueError("every window must have the same parameters")
+    dev = k_cache.device
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_win", k_win), ("v_win", v_win)):
+        _contig(n, t, k_cache.dtype, dev)
+    _contig("mask_state", mask_state, torch.uint8, dev)
+    _contig("tokens", tokens, torch.int32, dev)
+    _contig("block_phase", block_phase, torch.uint8, dev)
+    _contig("n_committed", n_committed, torch.int32, dev)
+    _contig("out_tokens", out_tokens, torch.int32, dev)
+    block_size = params.block_size if nb else 1
+    wmax = kw0.shape[2]
+    desc = make_desc(nb, hkv, hkv, d, block_size, wmax // block_size, cap, k_cache.dtype)
+    if nb and (mask_state.numel() != nb * wmax or tokens.numel() != nb * wmax or
+               block_phase.numel() != nb * params.max_win_blocks or
+               n_committed.numel() != nb * params.max_win_blocks or
+               out_tokens.numel() != nb * params.total_blocks * block_size):
+        raise ValueError("slot buffers do not match batch, window and total_blocks")
+    states = (WindowState * max(1, nb))()
+    for i, w in enumerate(windows):
+        states[i] = w.state
+    pl = _i32_array(prefix_len)
+    pers = (ctypes.c_int32 * max(1, nb))()
+    app = (ctypes.c_int32 * max(1, nb))()
+    _check(load().d2f_decode_advance(
+        ctypes.byref(desc), n_layers, _ptr(k_cache), _ptr(v_cache), kc0.numel(), _ptr(k_win),
+        _ptr(v_win), kw0.numel(), ctypes.byref(params) if nb else None, states, pl,
+        _ptr(prefix_len_dev), _ptr(n_committed), _ptr(mask_state), _ptr(tokens),
+        _ptr(block_phase), _ptr(out_tokens), int(mask_token_id), pers, app, _stream(stream)))
+    for i, w in enumerate(windows):
+        w.state = states[i]
+        prefix_len[i] = int(pl[i])
+    return [pers[i] for i in range(nb)], [app[i] for i in range(nb)]
+

@@ -24,11 +24,11 @@ d2f_status_t fail(d2f_status_t st, const char* fmt, ...) {
   return st;
 }
 
-namespace {
-
 d2f_status_t hip_fail(hipError_t e, const char* what) {
   return fail(D2F_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+namespace {
 
 // Work-unit sizing.  The key tiles of a (request, KV head, query tile) group
 // may be cut into nsplit key ranges, one workgroup each, at the price of a
@@ -81,6 +81,8 @@ bool head_dim_supported(d2f_dtype_t dt, int d) {
   return false;
 }
 
+}  // namespace
+
 d2f_status_t check_desc(const d2f_attn_desc_t* d) {
   if (d == nullptr) return fail(D2F_ERR_INVALID_ARG, "desc is NULL");
   if (d->batch < 0) return fail(D2F_ERR_INVALID_ARG, "batch %d < 0", d->batch);
@@ -106,6 +108,8 @@ d2f_status_t check_desc(const d2f_attn_desc_t* d) {
     return fail(D2F_ERR_INVALID_ARG, "softmax_scale is not finite");
   return D2F_OK;
 }
+
+namespace {
 
 d2f_status_t check_lengths(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin) {
   if (d->batch == 0) return D2F_OK;

@@ -137,6 +137,8 @@ hipError_t launch_confidence_commit(const CommitArgs& a, bool vec4, hipStream_t 
 // Record a printf-style message as the calling thread's last error (read by
 // d2f_last_error) and return st.
 d2f_status_t fail(d2f_status_t st, const char* fmt, ...);
+d2f_status_t hip_fail(hipError_t e, const char* what);
+d2f_status_t check_desc(const d2f_attn_desc_t* d);
 
 struct KvArgs {
   void* kc;
@@ -149,5 +151,34 @@ struct KvArgs {
   int32_t* prefix_dev;
 };
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t s);
+
+// One decoding step's bookkeeping after the commit pass, for up to
+// kMaxReqPerLaunch requests (decode.hip).
+struct AdvReq {
+  uint64_t phase_bits;  // phase of window blocks 0..n_win_new-1 for the next pass
+  int32_t persisted;    // blocks leaving the window (appended to the cache)
+  int32_t prefix;       // cache length before the append
+  int32_t first;        // absolute index of the oldest window block before
+  int32_t n_win_old;    // window blocks before
+  int32_t n_win_new;    // window blocks after (persists and the append applied)
+  int32_t copy_base;    // first KV-copy workgroup of this request
+};
+struct AdvArgs {
+  void* kc;
+  void* vc;
+  const void* kw;
+  const void* vw;
+  int64_t cache_layer_stride, win_layer_stride;  // elements
+  int64_t cap;
+  uint8_t* mask_state;
+  int32_t* tokens;
+  uint8_t* block_phase;
+  int32_t* out_tokens;
+  int32_t* prefix_dev;
+  int32_t n_layers, hkv, head_dim, bsz, esize, wmax, max_win, total_blocks;
+  int32_t n_req, req0, n_copy_wgs, mask_token_id;
+  AdvReq req[kMaxReqPerLaunch];
+};
+hipError_t launch_decode_advance(const AdvArgs& a, hipStream_t s);
 
 }  // namespace d2f

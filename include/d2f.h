@@ -257,6 +257,61 @@ d2f_status_t d2f_window_after_commit(const d2f_window_params_t* params, d2f_wind
                                      const int32_t* n_committed, int32_t* persisted_out,
                                      int32_t* appended_out);
 
+/* ---- One decoding step's bookkeeping after the commit pass ----
+ *
+ * [D2F-review] section "쉽게 이해하기" (inference paragraph): the window of
+ * active blocks moves forward while later blocks are already being decoded.
+ * [D2F-wiki] section "운영 관점" (KV cache management): a block's completion
+ * is the signal to make its K/V permanent cache entries.
+ *
+ * Slot layout of the window state on the device: request b owns rows
+ * [b * Wmax, (b + 1) * Wmax) of mask_state (uint8) and tokens (int32), and
+ * window blocks [b * max_win_blocks, (b + 1) * max_win_blocks) of block_phase
+ * (uint8) and n_committed (int32).  The commit pass runs over all
+ * batch * Wmax rows; rows past a request's window are COMMITTED, so their
+ * logits are never read.  Before the first step the caller sets rows
+ * [0, block_size) of every slot MASKED and the rest COMMITTED, block_phase
+ * slot 0 AGGRESSIVE and the rest CONSERVATIVE, and calls d2f_window_init for
+ * every request.
+ *
+ * d2f_decode_advance, once per step after d2f_confidence_commit:
+ *   1. copies n_committed to the host and synchronises `stream` (the step's
+ *      one device-to-host transfer);
+ *   2. applies d2f_window_after_commit to every request's window (requests
+ *      whose blocks are all persisted are skipped);
+ *   3. enqueues one launch per 64 requests that, for each request with p
+ *      persisted blocks: appends window rows [0, p * block_size) of k_win /
+ *      v_win of every layer to cache slots [P, P + p * block_size) (byte copy,
+ *      as d2f_kv_commit); copies their tokens to
+ *      out_tokens[b][first * block_size ...] (out_tokens is
+ *      [batch][total_blocks * block_size] int32, the decoded sequence); moves
+ *      the remaining window rows of mask_state / tokens to the front of the
+ *      slot; sets an appended block's rows MASKED with tokens = mask_token_id
+ *      and rows past the window COMMITTED; writes every block_phase slot of
+ *      the request (past the window: CONSERVATIVE); stores P + p * block_size
+ *      into prefix_len_dev[b] when prefix_len_dev is not NULL;
+ *   4. updates windows_host, prefix_len_host, persisted_host[b] and
+ *      appended_host[b] (int32 [batch] each).
+ * k_win / v_win are read, not moved: the next model pass writes the window's
+ * K/V for the new layout.  desc and the layer strides are as for
+ * d2f_kv_commit; params must agree with desc on block_size and
+ * max_win_blocks.
+ * Errors: D2F_ERR_INVALID_ARG (as for d2f_kv_commit and
+ * d2f_window_after_commit, mismatched params, an inconsistent window state),
+ * D2F_ERR_CAPACITY (a persisted block does not fit the cache): the host state
+ * is unchanged and nothing was enqueued.  D2F_ERR_HIP: the transfer or a
+ * launch failed; the host state is unchanged, device buffers may be partly
+ * updated when batch > 64. */
+d2f_status_t d2f_decode_advance(const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache,
+                                void* v_cache, int64_t cache_layer_stride, const void* k_win,
+                                const void* v_win, int64_t win_layer_stride,
+                                const d2f_window_params_t* params, d2f_window_t* windows_host,
+                                int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                                const int32_t* n_committed, uint8_t* mask_state, int32_t* tokens,
+                                uint8_t* block_phase, int32_t* out_tokens, int32_t mask_token_id,
+                                int32_t* persisted_host, int32_t* appended_host,
+                                d2f_stream_t stream);
+
 /* Static text for a status code. */
 const char* d2f_status_string(d2f_status_t status);
 

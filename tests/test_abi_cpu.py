@@ -140,3 +140,41 @@ def test_confidence_commit_errors(lib):
     assert commit(lib, 32, 126464, 16, ws_bytes=out.value - 1) == WORKSPACE
     assert commit(lib, 32, 126464, 16, ws=None) == WORKSPACE
     assert commit(lib, 0, 126464, 16) == OK             # nothing to do
+
+
+def advance(lib, d, params, states, prefix, layers=1, stride=0, null_tokens=False):
+    n = max(1, len(states))
+    arr = (B.WindowState * n)(*states)
+    pl = (ctypes.c_int32 * n)(*prefix)
+    pers = (ctypes.c_int32 * n)()
+    app = (ctypes.c_int32 * n)()
+    st = lib.d2f_decode_advance(ctypes.byref(d), layers, FAKE, FAKE, stride, FAKE, FAKE, stride,
+                                ctypes.byref(params) if params is not None else None, arr, pl,
+                                None, FAKE, FAKE, None if null_tokens else FAKE, FAKE, FAKE, 7,
+                                pers, app, None)
+    return st, [arr[i].n_win for i in range(len(states))], list(pl)[:len(prefix)]
+
+
+def test_decode_advance_errors(lib):
+    """Argument errors return before the one device transfer; the host state
+    stays as it was."""
+    d = desc(batch=2, max_win_blocks=3, block_size=16, cache_capacity=200)
+    good = B.WindowParams(16, 3, 4, 0.25, 0.75)
+    s = B.WindowState()
+    assert lib.d2f_window_init(ctypes.byref(good), ctypes.byref(s)) == OK
+    # params disagree with the desc on block size / window blocks
+    assert advance(lib, d, B.WindowParams(8, 3, 4, 0.25, 0.75), [s, s], [0, 0])[0] == INVALID
+    assert advance(lib, d, B.WindowParams(16, 2, 4, 0.25, 0.75), [s, s], [0, 0])[0] == INVALID
+    assert b"differ" in lib.d2f_last_error()
+    assert advance(lib, d, None, [s, s], [0, 0])[0] == INVALID
+    assert advance(lib, d, good, [s, s], [0, 0], null_tokens=True)[0] == INVALID
+    assert advance(lib, d, good, [s, s], [0, 0], layers=0)[0] == INVALID
+    assert advance(lib, d, good, [s, s], [0, 0], layers=2, stride=5)[0] == INVALID
+    assert advance(lib, d, good, [s, s], [-1, 0])[0] == INVALID
+    bad = B.WindowState()
+    ctypes.memmove(ctypes.byref(bad), ctypes.byref(s), ctypes.sizeof(s))
+    bad.started = 3                     # first + n_win != started
+    assert advance(lib, d, good, [s, bad], [0, 0]) == (INVALID, [1, 1], [0, 0])
+    assert b"inconsistent" in lib.d2f_last_error()
+    # an empty batch is a no-op
+    assert advance(lib, desc(batch=0, max_win_blocks=3), good, [], [])[0] == OK

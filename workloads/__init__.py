@@ -258,3 +258,40 @@ def config_commit_inputs(cfg: dict, device="cpu", seed: int = 0) -> CommitInputs
 def total_rows(shape: AttnShape) -> int:
     """Window positions of the whole batch (the commit pass's row count)."""
     return sum(shape.win_rows(b) for b in range(shape.batch))
+
+
+# ---- Synthetic multi-step decoding (the active-window loop) ----
+
+def decode_rows(vocab: int, positions: Sequence[int], ages: Sequence[int], step: int,
+                seed: int = 0, std: float = 3.0) -> torch.Tensor:
+    """fp32 logits of window rows for one synthetic decoding step (CPU).
+
+    Row r belongs to absolute position positions[r] of a block that has been in
+    the window for ages[r] steps.  Entries ~ N(0, std) drawn from a generator
+    keyed by (seed, step, position); one column per position (fixed over
+    steps, drawn from (seed, position)) is raised above the row's largest
+    other entry by 1.5 * age + u, u ~ U(0, 2) from (seed, step, position), so
+    that positions grow more confident the longer their block is active."""
+    out = torch.empty((len(positions), vocab), dtype=torch.float32)
+    for r, (pos, age) in enumerate(zip(positions, ages)):
+        g = torch.Generator().manual_seed(int(seed) * 1_000_003 + int(step) * 7919 + int(pos) * 131)
+        row = torch.randn(vocab, generator=g) * std
+        gc = torch.Generator().manual_seed(int(seed) * 1_000_003 + 17 + int(pos) * 977)
+        col = int(torch.randint(0, vocab, (1,), generator=gc))
+        u = float(torch.rand(1, generator=g)) * 2.0
+        row[col] = -float("inf")
+        row[col] = float(row.max()) + 1.5 * int(age) + u
+        out[r] = row
+    return out
+
+
+def decode_window_kv(n_heads: int, head_dim: int, positions: Sequence[int], step: int, tid: int,
+                     seed: int = 0, dtype: str = "bf16") -> torch.Tensor:
+    """[n_heads][len(positions)][head_dim] ~ N(0, 1) for the window rows of one
+    synthetic decoding step (CPU), keyed by (seed, step, position, tensor)."""
+    out = torch.empty((n_heads, len(positions), head_dim), dtype=torch.float32)
+    for r, pos in enumerate(positions):
+        g = torch.Generator().manual_seed(int(seed) * 1_000_003 + int(step) * 7919 + int(pos) * 131
+                                          + 100_000 * int(tid))
+        out[:, r, :] = torch.randn((n_heads, head_dim), generator=g)
+    return out.to(_torch_dtype(dtype))
