@@ -48,6 +48,8 @@ def attn_bytes(sh):
     tot = 0.0
     for b in range(sh.batch):
         w = sh.win_rows(b)
+        if w == 0:
+            continue  # idle request: nothing is read
         tot += sh.n_heads_kv * (sh.prefix_len[b] + w) * sh.head_dim * 2 * s
         tot += 2 * sh.n_heads_q * w * sh.head_dim * s + sh.n_heads_q * w * 4
     return tot
@@ -56,7 +58,7 @@ def attn_bytes(sh):
 def attn_kv_bytes(sh):
     s = 4 if sh.dtype == "f32" else 2
     return float(sum(sh.n_heads_kv * (sh.prefix_len[b] + sh.win_rows(b)) * sh.head_dim * 2 * s
-                     for b in range(sh.batch)))
+                     for b in range(sh.batch) if sh.win_rows(b) > 0))
 
 
 def commit_bytes(n_masked, rows, vocab):
@@ -82,6 +84,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="time complete multi-step decodes (pipelined active window) instead")
+    ap.add_argument("--loop-blocks", type=int, default=8, help="blocks decoded per request")
+    ap.add_argument("--loop-window", type=int, default=4, help="most blocks in the window")
+    ap.add_argument("--loop-reps", type=int, default=3, help="timed complete decodes")
+    ap.add_argument("--tau-add", type=float, default=0.25)
+    ap.add_argument("--tau-act", type=float, default=0.75)
     ap.add_argument("--summarize-counters", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE",
                                                               "RUN_FETCH", "RUN_WRITE"),
                     help="turn four rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of "
@@ -404,6 +413,189 @@ def cpu_baseline(wl, budget_s):
                         f"host affinity {len(os.sched_getaffinity(0))} cpus"))
 
 
+LOOP_METRIC = "D2F pipelined decoding: hot-path decoded tokens/s, LLaDA-8B shape"
+
+
+class DecodeLoop:
+    """Complete multi-step decodes of the batched ragged LLaDA-8B-shaped
+    workload (16 requests, prompts ~ U(256, 4096), 32 layers x 32 heads x
+    128, B = 16, vocab 126464) with the active-window schedule: per step,
+    attention of every layer over each request's window, the commit pass
+    over every window slot, and d2f_decode_advance (the step's one
+    device-to-host transfer).  Q, the window K/V and the logits are resident
+    synthetic tensors (the model that would produce them is not part of the
+    path); the logits rotate through a pool of independent N(0, 3) sets with
+    one boosted column per row, so every row's confidence is redrawn each
+    step."""
+
+    def __init__(self, args):
+        import torch
+        import workloads as W
+        import block_causal_attention_d2f_amd as d2f
+        self.cfg = cfg = W.config("cfg3")
+        sh = cfg["shape"]
+        self.nb, self.hq, self.hkv, self.d, self.B = (sh.batch, sh.n_heads_q, sh.n_heads_kv,
+                                                      sh.head_dim, sh.block_size)
+        self.L, self.vocab = cfg["layers"], cfg["vocab"]
+        self.mw, self.total = args.loop_window, args.loop_blocks
+        self.tau, self.k_aggr = cfg["taus"][0], cfg["k_aggr"]
+        self.tau_add, self.tau_act = args.tau_add, args.tau_act
+        self.prompt = list(sh.prefix_len)
+        self.cap = max(self.prompt) + self.total * self.B
+        self.wmax = self.mw * self.B
+        self.mask_id = self.vocab
+        dev = "cuda"
+        g = torch.Generator(device=dev).manual_seed(1234)
+        bf = torch.bfloat16
+
+        def randn(*shape):
+            return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(bf)
+        L, nb, hq, hkv, d = self.L, self.nb, self.hq, self.hkv, self.d
+        self.kc = torch.empty((L, nb, hkv, self.cap, d), dtype=bf, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        for l in range(L):  # layer by layer keeps the fp32 staging small
+            self.kc[l] = randn(nb, hkv, self.cap, d)
+            self.vc[l] = randn(nb, hkv, self.cap, d)
+        self.q = randn(L, nb, hq, self.wmax, d)
+        self.kw = randn(L, nb, hkv, self.wmax, d)
+        self.vw = randn(L, nb, hkv, self.wmax, d)
+        self.out = torch.empty((nb, hq, self.wmax, d), dtype=bf, device=dev)
+        self.lse = torch.empty((nb, hq, self.wmax), dtype=torch.float32, device=dev)
+        rows = nb * self.wmax
+        self.pool = [W.logits_normal(rows, self.vocab, cfg["logit_std"], True, device=dev,
+                                     seed=100 + r) for r in range(3)]
+        desc = d2f.make_desc(nb, hq, hkv, d, self.B, self.mw, self.cap, bf)
+        need = d2f.d2f_block_attn_workspace_size(desc, [max(self.prompt)] * nb, [self.mw] * nb)
+        self.ws_attn = torch.empty(max(need, 1 << 20) * 4, dtype=torch.uint8, device=dev)
+        self.ws_commit = torch.empty(d2f.d2f_confidence_commit_workspace_size(rows, self.vocab),
+                                     dtype=torch.uint8, device=dev)
+        self.ms = torch.empty(rows, dtype=torch.uint8, device=dev)
+        self.tk = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.ph = torch.empty(nb * self.mw, dtype=torch.uint8, device=dev)
+        self.ncd = torch.empty(nb * self.mw, dtype=torch.int32, device=dev)
+        self.bcd = torch.empty(nb * self.mw, dtype=torch.uint8, device=dev)
+        self.outt = torch.empty((nb, self.total * self.B), dtype=torch.int32, device=dev)
+        self.prefix_dev = torch.empty(nb, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def reset(self):
+        import torch
+        import block_causal_attention_d2f_amd as d2f
+        ms = torch.full((self.nb, self.wmax), d2f.COMMITTED, dtype=torch.uint8)
+        ms[:, :self.B] = d2f.MASKED
+        self.ms.copy_(ms.reshape(-1))
+        self.tk.fill_(self.mask_id)
+        ph = torch.zeros((self.nb, self.mw), dtype=torch.uint8)
+        ph[:, 0] = d2f.AGGRESSIVE
+        self.ph.copy_(ph.reshape(-1))
+        self.outt.fill_(-1)
+        self.P = list(self.prompt)
+        self.prefix_dev.copy_(torch.tensor(self.P, dtype=torch.int32))
+        self.wins = [d2f.Window(self.B, self.mw, self.total, self.tau_add, self.tau_act)
+                     for _ in range(self.nb)]
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        import block_causal_attention_d2f_amd as d2f
+        nwin = [w.n_win for w in self.wins]
+        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        rec(0)
+        for l in range(self.L):
+            d2f.d2f_block_attn(self.q[l], self.kc[l], self.vc[l], self.kw[l], self.vw[l], self.P,
+                               nwin, self.B, out=self.out, lse=self.lse, workspace=self.ws_attn)
+        rec(1)
+        d2f.d2f_confidence_commit(self.pool[i % len(self.pool)], self.ms, self.tk, self.ph,
+                                  self.B, self.tau, self.k_aggr, self.mask_id, n_committed=self.ncd,
+                                  block_complete=self.bcd, workspace=self.ws_commit,
+                                  want_conf=False)
+        rec(2)
+        d2f.d2f_decode_advance(self.kc, self.vc, self.kw, self.vw, self.wins, self.P, self.ncd,
+                               self.ms, self.tk, self.ph, self.outt, self.mask_id,
+                               prefix_len_dev=self.prefix_dev)
+        rec(3)
+        return nwin
+
+    def decode(self, events=False):
+        """One complete decode; returns the per-step windows and events."""
+        import torch
+        self.reset()
+        steps = []
+        while not all(w.done for w in self.wins):
+            if len(steps) > 100 * self.total:
+                raise RuntimeError("decoding did not finish")
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if events else None
+            prefix = list(self.P)
+            nwin = self.step(len(steps), ev)
+            steps.append((prefix, nwin, ev))
+        torch.cuda.synchronize()
+        return steps
+
+
+def decode_loop_main(args):
+    import torch
+    import workloads as W
+    lp = DecodeLoop(args)
+    lp.decode()                                   # warm-up decode (untimed)
+    outs = lp.outt.clone()
+    walls, n_steps = [], []
+    for _ in range(args.loop_reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st = lp.decode()
+        walls.append(time.perf_counter() - t0)
+        n_steps.append(len(st))
+        assert torch.equal(lp.outt, outs), "decodes of the same inputs differ"
+    assert (outs >= 0).all() and (outs != lp.mask_id).all(), "undecoded positions left"
+    # One more decode with events around the three phases of every step.
+    st = lp.decode(events=True)
+    t_attn = t_commit = t_adv = 0.0
+    a_bytes = a_flops = 0.0
+    for prefix, nwin, ev in st:
+        t_attn += ev[0].elapsed_time(ev[1]) * 1e-3
+        t_commit += ev[1].elapsed_time(ev[2]) * 1e-3
+        t_adv += ev[2].elapsed_time(ev[3]) * 1e-3
+        sh = W.make_shape(lp.nb, lp.hq, lp.hkv, lp.d, lp.B, prefix, nwin, dtype="bf16",
+                          max_win_blocks=lp.mw, cache_capacity=lp.cap)
+        a_bytes += attn_bytes(sh) * lp.L
+        a_flops += attn_flops(sh) * lp.L
+    tokens = lp.nb * lp.total * lp.B
+    wall = sum(walls) / len(walls)
+    steps = sum(n_steps) / len(n_steps)
+    attn_gbs = a_bytes / t_attn / 1e9
+    rec = {
+        "metric": LOOP_METRIC,
+        "value": round(tokens / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": int(round(steps)),
+        "warmup": 1,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "pipelined decoding of the batched ragged LLaDA-8B-shaped batch",
+                   "batch": lp.nb, "heads_q": lp.hq, "heads_kv": lp.hkv, "head_dim": lp.d,
+                   "layers": lp.L, "block_size": lp.B, "blocks_per_request": lp.total,
+                   "max_window_blocks": lp.mw, "prompt_len": f"U(256, 4096), mean "
+                   f"{sum(lp.prompt) / lp.nb:.0f}", "vocab": lp.vocab, "tau": lp.tau,
+                   "k_aggr": lp.k_aggr, "tau_add": lp.tau_add, "tau_act": lp.tau_act,
+                   "timed_decodes": args.loop_reps, "launch": "eager"},
+        "tokens_per_decode": tokens,
+        "tokens_per_step": round(tokens / steps, 2),
+        "wall_s_per_decode": round(wall, 5),
+        "phase_ms_per_step": {"attention_all_layers": round(t_attn / len(st) * 1e3, 4),
+                              "commit": round(t_commit / len(st) * 1e3, 4),
+                              "advance_incl_sync": round(t_adv / len(st) * 1e3, 4)},
+        "roofline": {"kernel": "d2f_block_attn", "bound": "hbm", "achieved": round(attn_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "tflops": round(a_flops / t_attn / 1e12, 3)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -420,6 +612,9 @@ def main():
         return
     import block_causal_attention_d2f_amd as d2f
     d2f.load()
+    if args.decode_loop:
+        decode_loop_main(args)
+        return
     K, Wu = args.steps, args.warmup
     n_masks = Wu + K + args.call_reps + 1
     wl = Workload(args.config, args.block_size, n_masks)

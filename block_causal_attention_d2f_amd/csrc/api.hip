@@ -117,8 +117,8 @@ d2f_status_t check_lengths(const d2f_attn_desc_t* d, const int32_t* prefix, cons
     return fail(D2F_ERR_INVALID_ARG, "prefix_len_host / n_win_blocks_host is NULL");
   for (int b = 0; b < d->batch; ++b) {
     if (prefix[b] < 0) return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d < 0", b, prefix[b]);
-    if (nwin[b] < 1 || nwin[b] > d->max_win_blocks)
-      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [1, %d]", b, nwin[b],
+    if (nwin[b] < 0 || nwin[b] > d->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b, nwin[b],
                   d->max_win_blocks);
     const long long need = (long long)prefix[b] + (long long)nwin[b] * d->block_size;
     if (need > d->cache_capacity)
@@ -180,6 +180,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
     const int b1 = std::min(d->batch, b0 + kMaxReqPerLaunch);
     std::vector<std::pair<long long, ReqInfo>> reqs;
     for (int b = b0; b < b1; ++b) {
+      if (nwin[b] == 0) continue;  // idle request: no query rows
       ReqInfo r{};
       r.b = b;
       r.prefix = prefix[b];
@@ -206,6 +207,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
       L.n_groups += d->n_heads_kv * r.qtiles;
       L.req.push_back(r);
     }
+    if (L.n_units == 0) continue;
     if (L.any_split) ws = std::max(ws, attn_partial_bytes(L, d->head_dim));
     out.push_back(std::move(L));
   }

@@ -114,7 +114,8 @@ d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
  *   k_win, v_win    [batch][n_heads_kv][Wmax][head_dim]
  *   lse             [batch][n_heads_q][Wmax] float, or NULL
  *   prefix_len_host [batch], 0 <= P and P + W <= cache_capacity
- *   n_win_blocks_host [batch], 1 <= n <= max_win_blocks
+ *   n_win_blocks_host [batch], 0 <= n <= max_win_blocks (0: the request is
+ *                   idle in this call, e.g. finished, and costs nothing)
  * Rows i >= W of out and lse are left untouched; cache slots >= P and window
  * rows >= W are never read.  workspace: >= d2f_block_attn_workspace_size
  * bytes of device memory, 256-byte aligned (may be NULL when that is 0).

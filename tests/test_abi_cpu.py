@@ -75,7 +75,8 @@ def test_attention_argument_errors(lib):
     assert lib.d2f_block_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, 0,
                               None) == INVALID
     assert attn(lib, desc(n_heads_q=3), [10], [1]) == INVALID          # group mismatch
-    assert attn(lib, desc(), [10], [0]) == INVALID                     # empty window
+    assert attn(lib, desc(), [10], [-1]) == INVALID                    # negative window
+    assert attn(lib, desc(), [10], [0]) == OK                          # idle request: no work
     assert attn(lib, desc(), [10], [4]) == INVALID                     # > max_win_blocks
     assert attn(lib, desc(), [-1], [1]) == INVALID
     assert attn(lib, desc(), [60], [3]) == CAPACITY                    # 60 + 48 > 100

@@ -45,6 +45,19 @@ def test_edge_shapes(dtype, case):
     _check(shape, seed=sum(prefix) + b, label=f"edge-{dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_idle_requests(dtype):
+    """n_win_blocks = 0 marks a request idle: its rows stay untouched and the
+    others are computed as usual; a batch of idle requests launches nothing."""
+    shape = W.make_shape(3, 4, 2, 64, 16, [50, 300, 7], [2, 0, 1], dtype=dtype,
+                         extra_capacity=3)
+    _check(shape, seed=11, label=f"idle-{dtype}")
+    shape = W.make_shape(2, 2, 2, 128, 16, [40, 9], [0, 0], dtype=dtype, max_win_blocks=2)
+    x = poisoned_inputs(shape, seed=12)
+    out, lse = run_attn(shape, x, out_fill=7.0)
+    assert (out.float() == 7.0).all() and (lse == 7.0).all()
+
+
 def test_fp32_head_dim_32_long_prefix():
     shape = W.make_shape(2, 2, 2, 32, 16, [2100, 33], [3, 2], dtype="f32")
     _check(shape, label="f32-d32-split")

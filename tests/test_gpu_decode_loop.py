@@ -64,7 +64,7 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
     while not all(w.done for w in owins):
         assert step < 60 * total, "decoding did not finish"
         live = [b for b in range(nb) if not owins[b].done]
-        nwin = [max(1, owins[b].n_win) for b in range(nb)]
+        nwin = [owins[b].n_win for b in range(nb)]   # 0 once a request is finished (idle)
         # -- attention, every layer ----------------------------------------------------
         for l in range(layers):
             for b in live:
@@ -73,8 +73,7 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
                 q[l, b, :, :len(pos)] = W.decode_window_kv(hq, d, pos, step, 1, seed=s).to(dev)
                 kw[l, b, :, :len(pos)] = W.decode_window_kv(hkv, d, pos, step, 2, seed=s).to(dev)
                 vw[l, b, :, :len(pos)] = W.decode_window_kv(hkv, d, pos, step, 3, seed=s).to(dev)
-            # finished requests keep one (stale) block of attention: the caller's choice
-            pl_attn = [P[b] if not owins[b].done else 0 for b in range(nb)]
+            pl_attn = list(P)
             d2f.d2f_block_attn(q[l], kc[l], vc[l], kw[l], vw[l], pl_attn, nwin, B, out=out,
                                lse=lse)
             torch.cuda.synchronize()
