@@ -184,16 +184,22 @@ def summarize_counters(args):
     print(path)
 
 
+# Sources the three per-step calls are built from (planner, kernels, shared
+# declarations); the multi-step bookkeeping (window.hip, decode.hip) is not
+# among them.
+STEP_SOURCES = ("api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_merge.h", "attn_merge.hip",
+                "commit.hip", "kv_commit.hip", "d2f_internal.h")
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources: counter-derived traffic is only reported for
-    the build it was measured on."""
+    """Hash of the HIP sources of the per-step calls: counter-derived traffic
+    is only reported for the build it was measured on."""
     import hashlib
     h = hashlib.sha256()
     d = os.path.join(ROOT, "block_causal_attention_d2f_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in STEP_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 

@@ -13,12 +13,21 @@
 // [b * max_win, (b + 1) * max_win) of block_phase / n_committed.  Rows past
 // the window are kept COMMITTED, so the commit pass does not read their logits.
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "d2f_internal.h"
 
 namespace d2f {
 namespace {
+
+constexpr int kCopySlices = 8;  // (layer, KV head, K or V) slices per copy workgroup
+constexpr int kCopyUnroll = 4;  // loads in flight per thread
+
+// Copy workgroups of a request that persists blocks.
+int copy_workgroups(int n_layers, int hkv) {
+  return (2 * n_layers * hkv + kCopySlices - 1) / kCopySlices;
+}
 
 __device__ int copy_request(const AdvArgs& a, int c) {
   // Last request whose first copy workgroup is <= c (requests without a copy
@@ -31,34 +40,48 @@ __device__ int copy_request(const AdvArgs& a, int c) {
   return lo;
 }
 
-// Workgroup c of the copy range: one (layer, KV head, K or V) of one request;
-// the persisted blocks are window rows [0, p * B), contiguous per head, and go
-// to cache slots [P, P + p * B).
+// Copy workgroup c: kCopySlices consecutive (layer, KV head, K or V) slices
+// of one request.  The persisted blocks are window rows [0, p * B), contiguous
+// per head, and go to cache slots [P, P + p * B).  Each thread keeps kCopyUnroll
+// loads in flight before it stores.
 template <bool VEC16>
 __device__ void copy_blocks(const AdvArgs& a, int c) {
+  using T = typename std::conditional<VEC16, uint4, uint16_t>::type;
   const int i = copy_request(a, c);
   const AdvReq& r = a.req[i];
   const size_t rb = (size_t)(a.req0 + i);
-  const int idx = c - r.copy_base;
-  const int which = idx & 1;
-  const int lh = idx >> 1;
-  const int layer = lh / a.hkv, head = lh % a.hkv;
+  const int n_slices = 2 * a.n_layers * a.hkv;
+  const int s0 = (c - r.copy_base) * kCopySlices;
+  const int s1 = min(n_slices, s0 + kCopySlices);
   const size_t esz = (size_t)a.esize;
-  const size_t nbytes = (size_t)r.persisted * a.bsz * a.head_dim * esz;
-  const char* src = (const char*)(which ? a.vw : a.kw) +
-                    ((size_t)layer * a.win_layer_stride +
-                     (rb * a.hkv + head) * (size_t)a.wmax * a.head_dim) * esz;
-  char* dst = (char*)(which ? a.vc : a.kc) +
-              ((size_t)layer * a.cache_layer_stride +
-               ((rb * a.hkv + head) * (size_t)a.cap + r.prefix) * a.head_dim) * esz;
-  if (VEC16) {
-    const uint4* s4 = (const uint4*)src;
-    uint4* d4 = (uint4*)dst;
-    for (size_t e = threadIdx.x; e < nbytes / 16; e += blockDim.x) d4[e] = s4[e];
-  } else {
-    const uint16_t* s2 = (const uint16_t*)src;
-    uint16_t* d2 = (uint16_t*)dst;
-    for (size_t e = threadIdx.x; e < nbytes / 2; e += blockDim.x) d2[e] = s2[e];
+  const uint32_t n = (uint32_t)((size_t)r.persisted * a.bsz * a.head_dim * esz / sizeof(T));
+  const uint32_t total = (uint32_t)(s1 - s0) * n;
+  for (uint32_t f0 = threadIdx.x; f0 < total; f0 += blockDim.x * kCopyUnroll) {
+    T v[kCopyUnroll];
+    T* dst[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint32_t f = f0 + (uint32_t)u * blockDim.x;
+      dst[u] = nullptr;
+      if (f < total) {
+        const int sl = s0 + (int)(f / n);
+        const uint32_t e = f % n;
+        const int which = sl & 1;
+        const int lh = sl >> 1;
+        const int layer = lh / a.hkv, head = lh % a.hkv;
+        const T* src = (const T*)((const char*)(which ? a.vw : a.kw) +
+                                  ((size_t)layer * a.win_layer_stride +
+                                   (rb * a.hkv + head) * (size_t)a.wmax * a.head_dim) * esz);
+        T* d = (T*)((char*)(which ? a.vc : a.kc) +
+                    ((size_t)layer * a.cache_layer_stride +
+                     ((rb * a.hkv + head) * (size_t)a.cap + r.prefix) * a.head_dim) * esz);
+        v[u] = src[e];
+        dst[u] = d + e;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u)
+      if (dst[u] != nullptr) *dst[u] = v[u];
   }
 }
 
@@ -169,6 +192,11 @@ extern "C" d2f_status_t d2f_decode_advance(
     return fail(D2F_ERR_INVALID_ARG, "layer strides smaller than one layer");
   if ((long long)params->total_blocks * B > (1LL << 30))
     return fail(D2F_ERR_INVALID_ARG, "total_blocks * block_size too large");
+  // A copy workgroup indexes its kCopySlices slices of at most Wmax rows with
+  // 32-bit counters of 2-byte elements.
+  if ((unsigned long long)wmax * desc->head_dim * (desc->dtype == D2F_BF16 ? 2 : 4) / 2 *
+          kCopySlices >= (1ULL << 32))
+    return fail(D2F_ERR_UNSUPPORTED, "window too large for the append copy");
   for (int b = 0; b < nb; ++b) {
     const d2f_window_t& w = windows_host[b];
     if (prefix_len_host[b] < 0)
@@ -238,7 +266,7 @@ extern "C" d2f_status_t d2f_decode_advance(
       for (int k = 0; k < r.n_win_new; ++k)
         if (win[b].phase[k] == D2F_AGGRESSIVE) r.phase_bits |= 1ull << k;
       r.copy_base = copies;
-      if (r.persisted > 0) copies += 2 * n_layers * desc->n_heads_kv;
+      if (r.persisted > 0) copies += copy_workgroups(n_layers, desc->n_heads_kv);
     }
     a.n_copy_wgs = copies;
     e = launch_decode_advance(a, (hipStream_t)stream);
