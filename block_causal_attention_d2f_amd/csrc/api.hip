@@ -37,11 +37,15 @@ namespace {
 // (a long prefix among short ones, or too few groups to occupy the device).
 // With C = total key tiles / (kSlotFill x resident workgroups), a request is
 // split, into ceil(tiles / C) ranges, only if its longest query tile has more
-// than kSplitFactor x C tiles.  (Measured on MI355X, bf16 head_dim 128: with
-// 512 or more groups any split was slower; with 32 groups, 256 to 512 units
-// were within 3% of the best for a 32K prefix, and no split was best for a
-// 512-token prefix.)  Units never get shorter than kMinChunkTiles tiles.
-constexpr int kMinChunkTiles = 8;
+// than kSplitFactor x C tiles.  Units never get shorter than kMinChunkTiles
+// tiles.  (Measured on MI355X, bf16 head_dim 128: with 512 or more groups any
+// split was slower; with 32 groups, 256 to 512 units were within 3% of the
+// best for a 32K prefix.  A workgroup keeps one key tile in flight, so a
+// launch with few groups is bound by load latency, about 1.5 us per tile:
+// with 32 heads and a 512- or 1024-token prefix, chunks of 3 tiles took 11%
+// and 18% off, with 8 heads and 2048 tokens 25%; 1-2 tile chunks lost the
+// gain to the merge.)
+constexpr int kMinChunkTiles = 3;
 constexpr double kSlotFill = 0.75;
 constexpr long long kSplitFactor = 2;
 constexpr int kDefaultCUs = 256;        // MI355X, used when no device is visible
