@@ -41,8 +41,10 @@ Readings taken where the pages are silent:
   * every measure drives the same block rule (conf > tau; aggressive blocks
     also take the k_aggr largest); the second-largest logit counts a repeated
     maximum again (two equal maxima: margin 0, gap 0);
-  * Prophet's early commit is evaluated per group of consecutive blocks (one
-    request's window): it fires when the smallest logit gap over the group's
+  * Prophet's early commit tests the logit gap whatever measure drives the
+    ordinary rule (Prophet sits on top of the model's own decoder); it is
+    evaluated per group of consecutive blocks (one request's window): it
+    fires when the smallest logit gap over the group's
     positions that were MASKED on entry is strictly above the group's
     threshold, after the ordinary rule has run, and commits the group's
     remaining MASKED positions with their argmax; its threshold steps are
@@ -134,10 +136,11 @@ def confidence_commit(logits, mask_state, tokens, block_phase, block_size, tau, 
     """One commit pass over a window (several requests' blocks concatenated).
 
     logits [n_rows][V]; mask_state, tokens [n_rows]; block_phase [n_rows/B].
-    ``measure`` names the confidence (see row_measures).  ``early_gap``
-    (measure "logit_gap" only): per-group thresholds of Prophet's early
-    commit, groups of ``early_group_blocks`` consecutive blocks (0: one
-    group); None disables it.
+    ``measure`` names the confidence (see row_measures).  ``early_gap``:
+    per-group thresholds of Prophet's early commit (tested on the logit gap
+    whatever the measure; not with "neg_entropy"), groups of
+    ``early_group_blocks`` consecutive blocks (0: one group); None disables
+    it.
     Returns a dict with the updated mask_state (uint8) and tokens (int64),
     conf (fp64; NaN for rows COMMITTED on entry), argmax (-1 likewise),
     n_committed and block_complete per block, early (per group: 1 when the
@@ -197,7 +200,7 @@ def confidence_commit(logits, mask_state, tokens, block_phase, block_size, tau, 
     early = np.zeros(n_groups, dtype=np.uint8)
     near_early = np.zeros(n_groups, dtype=bool)
     if early_gap is not None:
-        assert measure == "logit_gap"
+        assert measure != "neg_entropy"
         thr = np.broadcast_to(np.asarray(early_gap, dtype=np.float32).astype(np.float64),
                               (n_groups,))
         for g in range(n_groups):

@@ -136,3 +136,20 @@ def test_prophet_hand_worked_fixture(name):
 def test_prophet_threshold_steps():
     assert [OC.prophet_threshold(p) for p in (0.0, 0.2, 0.34, 0.5, 0.67, 0.9, 1.0)] == \
         [7.5, 7.5, 5.0, 5.0, 2.5, 2.5, 2.5]
+
+
+def test_prophet_on_top_of_max_probability():
+    """The early test reads the logit gap while max probability drives the
+    ordinary rule (tau 2 lets nothing through on its own)."""
+    rows = _read_cases()["A"]["rows"]
+    logits = np.array([[float(v) for v in r[3:7]] for r in rows], np.float32)
+    out = OC.confidence_commit(logits, np.zeros(4, np.uint8), np.full(4, 99), np.zeros(2, np.uint8),
+                               2, 2.0, 0, 99, measure="maxprob", early_gap=[2.5, 2.5],
+                               early_group_blocks=1)
+    assert list(out["mask_state"]) == [C, C, M, M]
+    assert list(out["tokens"]) == [0, 1, 99, 99]
+    assert list(out["n_committed"]) == [2, 0] and list(out["block_complete"]) == [1, 0]
+    assert list(out["early"]) == [1, 0]
+    with pytest.raises(AssertionError):
+        OC.confidence_commit(logits, np.zeros(4, np.uint8), np.full(4, 99), np.zeros(2, np.uint8),
+                             2, 2.0, 0, 99, measure="neg_entropy", early_gap=2.5)
