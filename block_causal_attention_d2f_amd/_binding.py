@@ -27,9 +27,11 @@ CONSERVATIVE, AGGRESSIVE = 0, 1
 
 EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
+           "d2f_confidence_commit_ex", "d2f_prophet_threshold",
            "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
            "d2f_status_string", "d2f_last_error", "d2f_version")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
+MEASURES = {"maxprob": 0, "margin": 1, "neg_entropy": 2, "logit_gap": 3}  # d2f_conf_measure_t
 
 
 class D2FError(RuntimeError):
@@ -85,6 +87,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "d2f_confidence_commit_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "d2f_confidence_commit": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _i32,
                                          _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "d2f_confidence_commit_ex": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32, _i32,
+                                            _f32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
+                                            _vp, _sz, _vp]),
+        "d2f_prophet_threshold": (_f32, [_f32]),
         "d2f_window_init": (_i32, [ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState)]),
         "d2f_window_after_commit": (_i32, [ctypes.POINTER(WindowParams),
                                            ctypes.POINTER(WindowState), _pi32, _pi32, _pi32]),
@@ -215,13 +221,20 @@ def d2f_confidence_commit_workspace_size(n_rows: int, vocab: int) -> int:
 def d2f_confidence_commit(logits, mask_state, tokens, block_phase, block_size: int, tau: float,
                           k_aggr: int = 1, mask_token_id: int = 0, conf_out=None,
                           argmax_out=None, n_committed=None, block_complete=None,
-                          workspace=None, stream=None, want_conf=True):
+                          workspace=None, stream=None, want_conf=True, measure="maxprob",
+                          early_gap=None, early_group_blocks: int = 0):
     """One commit pass.  logits [rows][V] fp32 (row stride may exceed V);
     mask_state uint8 [rows] and tokens int32 [rows] are updated in place.
+    ``measure``: "maxprob" (d2f_confidence_commit), "margin", "neg_entropy" or
+    "logit_gap" (d2f_confidence_commit_ex); ``early_gap``: Prophet's early
+    commit thresholds, one per group of ``early_group_blocks`` blocks (a
+    float, a sequence or a device float32 tensor), or None.
     Returns dict(n_committed, block_complete, conf, argmax)."""
     rows, vocab = logits.shape
     if logits.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
+    if measure not in MEASURES:
+        raise ValueError(f"unknown measure {measure!r}")
     dev = logits.device
     _contig("mask_state", mask_state, torch.uint8, dev)
     _contig("tokens", tokens, torch.int32, dev)
@@ -238,13 +251,36 @@ def d2f_confidence_commit(logits, mask_state, tokens, block_phase, block_size: i
     need = d2f_confidence_commit_workspace_size(rows, vocab)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    _check(load().d2f_confidence_commit(
-        _ptr(logits), logits.stride(0), rows, vocab, _ptr(mask_state), _ptr(tokens),
-        _ptr(block_phase), int(block_size), ctypes.c_float(tau), int(k_aggr), int(mask_token_id),
-        _ptr(conf_out), _ptr(argmax_out), _ptr(n_committed), _ptr(block_complete),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    gb = min(early_group_blocks, n_blocks) if early_group_blocks > 0 else max(n_blocks, 1)
+    n_groups = max(1, (n_blocks + gb - 1) // gb)
+    if early_gap is not None and not isinstance(early_gap, torch.Tensor):
+        vals = [float(early_gap)] * n_groups if isinstance(early_gap, (int, float)) \
+            else [float(v) for v in early_gap]
+        early_gap = torch.tensor(vals, dtype=torch.float32, device=dev)
+    if early_gap is not None:
+        _contig("early_gap", early_gap, torch.float32, dev)
+        if early_gap.numel() < n_groups:   # the kernels read one threshold per group
+            raise ValueError(f"early_gap holds {early_gap.numel()} thresholds for "
+                             f"{n_groups} groups")
+    args_tail = (_ptr(conf_out), _ptr(argmax_out), _ptr(n_committed), _ptr(block_complete),
+                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if measure == "maxprob" and early_gap is None:
+        _check(load().d2f_confidence_commit(
+            _ptr(logits), logits.stride(0), rows, vocab, _ptr(mask_state), _ptr(tokens),
+            _ptr(block_phase), int(block_size), ctypes.c_float(tau), int(k_aggr),
+            int(mask_token_id), *args_tail))
+    else:
+        _check(load().d2f_confidence_commit_ex(
+            _ptr(logits), logits.stride(0), rows, vocab, _ptr(mask_state), _ptr(tokens),
+            _ptr(block_phase), int(block_size), MEASURES[measure], ctypes.c_float(tau),
+            int(k_aggr), int(mask_token_id), _ptr(early_gap), int(early_group_blocks),
+            *args_tail))
     return dict(n_committed=n_committed, block_complete=block_complete, conf=conf_out,
                 argmax=argmax_out)
+
+
+def prophet_threshold(progress: float) -> float:
+    return float(load().d2f_prophet_threshold(ctypes.c_float(progress)))
 
 
 def version() -> int:

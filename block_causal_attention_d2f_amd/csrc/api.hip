@@ -224,8 +224,12 @@ size_t commit_chunks(int32_t vocab) { return (size_t)((vocab + kCommitChunk - 1)
 size_t commit_partial_bytes(int32_t n_rows, int32_t vocab) {
   return (size_t)n_rows * commit_chunks(vocab) * sizeof(float4);
 }
+// One int32 / uint32 word per row, rounded up to 16 bytes.
+size_t commit_row_words_bytes(int32_t n_rows) { return ((size_t)n_rows * 4 + 15) / 16 * 16; }
+// Partials, then the early commit's argmax per row and gap minimum per group
+// (at most one group per row).
 size_t commit_workspace_bytes(int32_t n_rows, int32_t vocab) {
-  return commit_partial_bytes(n_rows, vocab);
+  return commit_partial_bytes(n_rows, vocab) + 2 * commit_row_words_bytes(n_rows);
 }
 
 }  // namespace
@@ -396,13 +400,15 @@ d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
   return D2F_OK;
 }
 
-d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_rows,
-                                   int32_t vocab, uint8_t* mask_state, int32_t* tokens,
-                                   const uint8_t* block_phase, int32_t block_size, float tau,
-                                   int32_t k_aggr, int32_t mask_token_id, float* conf_out,
-                                   int32_t* argmax_out, int32_t* n_committed,
-                                   uint8_t* block_complete, void* workspace,
-                                   size_t workspace_bytes, d2f_stream_t stream) {
+d2f_status_t d2f_confidence_commit_ex(const float* logits, int64_t ld, int32_t n_rows,
+                                      int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                      const uint8_t* block_phase, int32_t block_size,
+                                      d2f_conf_measure_t measure, float tau, int32_t k_aggr,
+                                      int32_t mask_token_id, const float* early_gap,
+                                      int32_t early_group_blocks, float* conf_out,
+                                      int32_t* argmax_out, int32_t* n_committed,
+                                      uint8_t* block_complete, void* workspace,
+                                      size_t workspace_bytes, d2f_stream_t stream) {
   if (n_rows < 0 || vocab < 1 || ld < vocab)
     return fail(D2F_ERR_INVALID_ARG, "n_rows %d, vocab %d, ld %lld out of range", n_rows, vocab,
                 (long long)ld);
@@ -413,6 +419,13 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
     return fail(D2F_ERR_UNSUPPORTED, "block_size %d > %d", block_size, kMaxCommitBlock);
   if (k_aggr < 0) return fail(D2F_ERR_INVALID_ARG, "k_aggr %d < 0", k_aggr);
   if (std::isnan(tau)) return fail(D2F_ERR_INVALID_ARG, "tau is NaN");
+  if ((int)measure < (int)D2F_CONF_MAXPROB || (int)measure > (int)D2F_CONF_LOGIT_GAP)
+    return fail(D2F_ERR_INVALID_ARG, "unknown confidence measure %d", (int)measure);
+  if (early_group_blocks < 0)
+    return fail(D2F_ERR_INVALID_ARG, "early_group_blocks %d < 0", early_group_blocks);
+  if (early_gap != nullptr && measure == D2F_CONF_NEG_ENTROPY)
+    return fail(D2F_ERR_INVALID_ARG, "the early commit needs the logit gap, which the "
+                "negative-entropy pass does not keep");
   if (n_rows == 0) return D2F_OK;
   if (logits == nullptr || mask_state == nullptr || tokens == nullptr || block_phase == nullptr ||
       n_committed == nullptr || block_complete == nullptr)
@@ -426,6 +439,8 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
     return fail(D2F_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   if ((unsigned long long)n_rows * n_chunks > 0x7fffffffULL)
     return fail(D2F_ERR_UNSUPPORTED, "too many rows x chunks for one launch");
+  const int n_blocks = n_rows / block_size;
+  const int group = early_group_blocks == 0 ? n_blocks : std::min(early_group_blocks, n_blocks);
   CommitArgs a{};
   a.logits = logits;
   a.ld = ld;
@@ -445,10 +460,37 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
   a.n_committed = n_committed;
   a.block_complete = block_complete;
   a.partial = (float4*)workspace;
+  a.measure = (int32_t)measure;
+  a.group_blocks = group;
+  a.n_groups = (n_blocks + group - 1) / group;
+  a.early_gap = early_gap;
+  char* extra = (char*)workspace + commit_partial_bytes(n_rows, vocab);
+  a.ws_argmax = (int32_t*)extra;
+  a.ws_gmin = (uint32_t*)(extra + commit_row_words_bytes(n_rows));
   const bool vec4 = ((uintptr_t)logits % 16) == 0 && (ld % 4) == 0;
   hipError_t e = launch_confidence_commit(a, vec4, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "confidence commit launch");
   return D2F_OK;
+}
+
+d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_rows,
+                                   int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                   const uint8_t* block_phase, int32_t block_size, float tau,
+                                   int32_t k_aggr, int32_t mask_token_id, float* conf_out,
+                                   int32_t* argmax_out, int32_t* n_committed,
+                                   uint8_t* block_complete, void* workspace,
+                                   size_t workspace_bytes, d2f_stream_t stream) {
+  return d2f_confidence_commit_ex(logits, ld, n_rows, vocab, mask_state, tokens, block_phase,
+                                  block_size, D2F_CONF_MAXPROB, tau, k_aggr, mask_token_id,
+                                  nullptr, 0, conf_out, argmax_out, n_committed, block_complete,
+                                  workspace, workspace_bytes, stream);
+}
+
+float d2f_prophet_threshold(float progress) {
+  const float p = std::isnan(progress) ? 0.f : std::min(1.f, std::max(0.f, progress));
+  if (3.f * p < 1.f) return 7.5f;
+  if (3.f * p < 2.f) return 5.0f;
+  return 2.5f;
 }
 
 }  // extern "C"

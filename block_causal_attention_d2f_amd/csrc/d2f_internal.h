@@ -127,8 +127,16 @@ struct CommitArgs {
   int32_t* argmax_out;
   int32_t* n_committed;
   uint8_t* block_complete;
-  float4* partial;  // [row][chunk] = {max, sum, argmax bits, unused}
+  float4* partial;  // [row][chunk] = {max, sum, argmax bits, aux}
+  int32_t measure;       // d2f_conf_measure_t
+  int32_t group_blocks;  // blocks per early-commit group
+  int32_t n_groups;
+  const float* early_gap;  // [n_groups] thresholds, or nullptr: no early commit
+  int32_t* ws_argmax;      // [n_rows], early commit only
+  uint32_t* ws_gmin;       // [n_groups] bits of the smallest logit gap, early commit only
 };
+// Per-chunk auxiliary accumulator of the vocabulary pass.
+enum { kAuxNone = 0, kAuxSecond = 1, kAuxXlogx = 2 };
 constexpr int kCommitThreads = 256;
 constexpr int kCommitChunk = 8192;     // logits per workgroup (32 KiB)
 constexpr int kMaxCommitBlock = 1024;  // rows per D2F block handled by one workgroup

@@ -157,7 +157,8 @@ d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* 
                            int32_t block, int32_t* prefix_len_host, int32_t* prefix_len_dev,
                            d2f_stream_t stream);
 
-/* Bytes of device workspace d2f_confidence_commit needs. */
+/* Bytes of device workspace d2f_confidence_commit and d2f_confidence_commit_ex
+ * need (16-byte aligned; its contents need no initialisation). */
 d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
                                                   size_t* bytes_out);
 
@@ -201,6 +202,58 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
                                    int32_t* argmax_out, int32_t* n_committed,
                                    uint8_t* block_complete, void* workspace,
                                    size_t workspace_bytes, d2f_stream_t stream);
+
+/* ---- Other confidence measures and Prophet's early commit ----
+ *
+ * [dLLM-survey] section "신뢰도를 넘어서: 궤적 일관성 디코딩(CCD)": decoders
+ * choose positions by the local confidence or by the negative entropy of the
+ * predicted distribution; section "토큰 순서의 이론": the top-probability
+ * order (LLaDA's default) and the top-probability margin order, Dream using
+ * the negative entropy; section "답을 미리 안다: 조기 확정 디코딩(Prophet)":
+ * the confidence gap between the two largest logits, and once it passes a
+ * threshold (lowered 7.5, 5.0, 2.5 as decoding progresses) every remaining
+ * mask is filled with its argmax.
+ *
+ * With p = softmax(row) and l(1) >= l(2) the two largest logits (a repeated
+ * maximum counts twice):
+ *   D2F_CONF_MAXPROB      conf = max_j p_j                (d2f_confidence_commit)
+ *   D2F_CONF_MARGIN       conf = p(1) - p(2)
+ *   D2F_CONF_NEG_ENTROPY  conf = sum_j p_j ln p_j  (<= 0)
+ *   D2F_CONF_LOGIT_GAP    conf = l(1) - l(2)  (+inf for a one-entry row)
+ * Every measure reads each MASKED row once, as the maximum probability does.
+ */
+typedef enum {
+  D2F_CONF_MAXPROB = 0,
+  D2F_CONF_MARGIN = 1,
+  D2F_CONF_NEG_ENTROPY = 2,
+  D2F_CONF_LOGIT_GAP = 3
+} d2f_conf_measure_t;
+
+/* d2f_confidence_commit with a chosen measure (same block rule, buffers and
+ * errors; conf_out receives the measure) and, optionally, Prophet's early
+ * commit: early_gap (device, float [n_groups], or NULL for none) holds one
+ * threshold per group of early_group_blocks consecutive blocks (0: all blocks
+ * form one group; n_groups = ceil(n_blocks / group)).  After the block rule,
+ * a group whose smallest logit gap over the rows that were MASKED on entry is
+ * strictly above its threshold has every still-MASKED row committed with its
+ * argmax (n_committed includes them; block_complete becomes 1).  The early
+ * commit reads the logit gap under any measure except D2F_CONF_NEG_ENTROPY
+ * (D2F_ERR_INVALID_ARG).  Errors as d2f_confidence_commit, plus
+ * D2F_ERR_INVALID_ARG for an unknown measure or early_group_blocks < 0. */
+d2f_status_t d2f_confidence_commit_ex(const float* logits, int64_t ld, int32_t n_rows,
+                                      int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                      const uint8_t* block_phase, int32_t block_size,
+                                      d2f_conf_measure_t measure, float tau, int32_t k_aggr,
+                                      int32_t mask_token_id, const float* early_gap,
+                                      int32_t early_group_blocks, float* conf_out,
+                                      int32_t* argmax_out, int32_t* n_committed,
+                                      uint8_t* block_complete, void* workspace,
+                                      size_t workspace_bytes, d2f_stream_t stream);
+
+/* Prophet's threshold for a decoding progress in [0, 1] (clamped): 7.5 below
+ * 1/3, 5.0 below 2/3, 2.5 from there on (the pages give the three values,
+ * not where they change; thirds are this library's reading).  Host only. */
+float d2f_prophet_threshold(float progress);
 
 /* ---- Active-window schedule (host only; no device memory, no stream) ----
  *

@@ -63,7 +63,7 @@ NEAR_TIE = 1e-6
 MEASURES = ("maxprob", "margin", "neg_entropy", "logit_gap")
 # Width of the band around a threshold inside which fp32 and fp64 may decide
 # differently, per measure (see the design notes for the error bounds).
-NEAR = {"maxprob": 1e-6, "margin": 1e-6, "neg_entropy": 1e-4, "logit_gap": 1e-5}
+NEAR = {"maxprob": 1e-6, "margin": 1e-6, "neg_entropy": 5e-5, "logit_gap": 1e-5}
 PROPHET_STEPS = (7.5, 5.0, 2.5)
 
 
@@ -184,7 +184,8 @@ def confidence_commit(logits, mask_state, tokens, block_phase, block_size, tau, 
         if phase[k] == AGGRESSIVE and k_aggr > 0:
             order = sorted(cand, key=lambda p: (-conf[p], p))
             chosen |= set(order[:k_aggr])
-            if len(order) > k_aggr and abs(conf[order[k_aggr - 1]] - conf[order[k_aggr]]) <= band:
+            if len(order) > k_aggr and (conf[order[k_aggr - 1]] == conf[order[k_aggr]] or
+                                        abs(conf[order[k_aggr - 1]] - conf[order[k_aggr]]) <= band):
                 near_topk[k] = True
         for p in cand:
             if p in chosen:

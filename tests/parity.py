@@ -79,12 +79,14 @@ def compare_attn(shape, out, lse, ref_out, ref_lse, pairs=None, label=""):
     return stats
 
 
-def run_commit(ci, tau, k_aggr, device="cuda"):
+def run_commit(ci, tau, k_aggr, device="cuda", measure="maxprob", early_gap=None,
+               early_group_blocks=0):
     import block_causal_attention_d2f_amd as d2f
     ms = ci.mask_state.to(device).clone()
     tok = ci.tokens.to(device).clone()
     res = d2f.d2f_confidence_commit(ci.logits, ms, tok, ci.block_phase.to(device), ci.block_size,
-                                    tau, k_aggr, ci.mask_token_id)
+                                    tau, k_aggr, ci.mask_token_id, measure=measure,
+                                    early_gap=early_gap, early_group_blocks=early_group_blocks)
     torch.cuda.synchronize()
     return dict(mask_state=ms.cpu().numpy(), tokens=tok.cpu().numpy().astype(np.int64),
                 n_committed=res["n_committed"].cpu().numpy(),
@@ -93,21 +95,29 @@ def run_commit(ci, tau, k_aggr, device="cuda"):
                 argmax=res["argmax"].cpu().numpy().astype(np.int64))
 
 
-def compare_commit(ci, got, tau, k_aggr, blocks=None, label=""):
+def compare_commit(ci, got, tau, k_aggr, blocks=None, label="", measure="maxprob",
+                   early_gap=None, early_group_blocks=0):
     """Bit-exact comparison of argmax and every decision, except rows whose
-    fp64 confidence lies within 1e-6 of tau and aggressive blocks whose
-    k-th / (k+1)-th confidences are within 1e-6 (counted and reported).
-    ``blocks`` restricts the oracle to a subset of blocks."""
+    fp64 confidence lies within the measure's band (1e-6 for probabilities)
+    of tau, aggressive blocks whose k-th / (k+1)-th confidences are that
+    close, and early-commit groups whose smallest gap is that close to the
+    threshold (all counted and reported).  ``blocks`` restricts the oracle
+    to a subset of blocks (not with the early commit)."""
     B = ci.block_size
     n_blocks = ci.mask_state.shape[0] // B
+    assert blocks is None or early_gap is None
     blocks = list(range(n_blocks)) if blocks is None else list(blocks)
     rows = np.concatenate([np.arange(k * B, (k + 1) * B) for k in blocks])
     rows_t = torch.as_tensor(rows, device=ci.logits.device)
     ref = OC.confidence_commit(ci.logits.index_select(0, rows_t), ci.mask_state.cpu()[rows],
                                ci.tokens.cpu()[rows], ci.block_phase.cpu()[blocks], B, tau, k_aggr,
-                               ci.mask_token_id)
+                               ci.mask_token_id, measure=measure, early_gap=early_gap,
+                               early_group_blocks=early_group_blocks)
     near_row = ref["near_tau"].copy()
-    near_blk = ref["near_topk"]
+    near_blk = ref["near_topk"].copy()
+    gb = early_group_blocks if early_group_blocks else len(blocks)
+    for g in np.flatnonzero(ref["near_early"]):
+        near_blk[g * gb:(g + 1) * gb] = True
     for j in range(len(blocks)):
         if near_blk[j]:
             near_row[j * B:(j + 1) * B] = True
@@ -119,15 +129,20 @@ def compare_commit(ci, got, tau, k_aggr, blocks=None, label=""):
     assert (g["mask_state"][ok] == ref["mask_state"][ok]).all(), f"{label}: mask_state differs"
     assert (g["tokens"][ok] == ref["tokens"][ok]).all(), f"{label}: tokens differ"
     blk_ok = np.array([not near_row[j * B:(j + 1) * B].any() for j in range(len(blocks))], bool)
-    gb = np.array(blocks)
-    assert (got["n_committed"][gb][blk_ok] == ref["n_committed"][blk_ok]).all(), label
-    assert (got["block_complete"][gb][blk_ok] == ref["block_complete"][blk_ok]).all(), label
-    cerr = float(np.abs(g["conf"][live] - ref["conf"][live]).max()) if live.any() else 0.0
+    bsel = np.array(blocks)
+    assert (got["n_committed"][bsel][blk_ok] == ref["n_committed"][blk_ok]).all(), label
+    assert (got["block_complete"][bsel][blk_ok] == ref["block_complete"][blk_ok]).all(), label
+    fin = live & np.isfinite(ref["conf"])
+    cerr = float(np.abs(g["conf"][fin] - ref["conf"][fin]).max()) if fin.any() else 0.0
+    # a one-entry row has an infinite logit gap on both sides
+    assert (g["conf"][live & ~fin] == ref["conf"][live & ~fin]).all(), f"{label}: conf differs"
     stats = dict(rows=len(rows), live=int(live.sum()), near_tau=int(ref["near_tau"].sum()),
-                 near_topk=int(near_blk.sum()), conf_max_err=cerr,
+                 near_topk=int(ref["near_topk"].sum()), near_early=int(ref["near_early"].sum()),
+                 early=int(ref["early"].sum()), conf_max_err=cerr,
                  committed=int(ref["n_committed"].sum()))
     say(f"[commit {label}] {stats}")
-    assert cerr <= 1e-6, stats
+    # conf itself: within the measure's decision band (1e-6 for probabilities)
+    assert cerr <= OC.NEAR[measure], stats
     return stats
 
 

@@ -137,7 +137,8 @@ def test_confidence_commit_errors(lib):
     assert commit(lib, 32, 100, 16, tau=float("nan")) == INVALID
     out = ctypes.c_size_t(0)
     assert lib.d2f_confidence_commit_workspace_size(32, 126464, ctypes.byref(out)) == OK
-    assert out.value == 32 * 16 * 16                     # 16 chunks of 8192 logits, 16 B each
+    # 16 chunks of 8192 logits, 16 B each, then the early commit's two words per row
+    assert out.value == 32 * 16 * 16 + 2 * 32 * 4
     assert commit(lib, 32, 126464, 16, ws_bytes=out.value - 1) == WORKSPACE
     assert commit(lib, 32, 126464, 16, ws=None) == WORKSPACE
     assert commit(lib, 0, 126464, 16) == OK             # nothing to do
@@ -179,3 +180,25 @@ def test_decode_advance_errors(lib):
     assert b"inconsistent" in lib.d2f_last_error()
     # an empty batch is a no-op
     assert advance(lib, desc(batch=0, max_win_blocks=3), good, [], [])[0] == OK
+
+
+def commit_ex(lib, measure, early=None, group=0, rows=32, vocab=100, bsz=16):
+    return lib.d2f_confidence_commit_ex(FAKE, vocab, rows, vocab, FAKE, FAKE, FAKE, bsz, measure,
+                                        ctypes.c_float(0.9), 1, 0, early, group, None, None, FAKE,
+                                        FAKE, FAKE, 1 << 30, None)
+
+
+def test_confidence_commit_ex_errors(lib):
+    assert commit_ex(lib, 4) == INVALID                              # unknown measure
+    assert commit_ex(lib, -1) == INVALID
+    assert commit_ex(lib, 2, early=FAKE) == INVALID                  # entropy keeps no gap
+    assert b"gap" in lib.d2f_last_error()
+    assert commit_ex(lib, 3, early=FAKE, group=-1) == INVALID
+    assert commit_ex(lib, 1, rows=30) == INVALID                     # rows not a multiple of B
+    assert commit_ex(lib, 3, rows=0) == OK                           # nothing to do
+
+
+def test_prophet_threshold_steps(lib):
+    f = lib.d2f_prophet_threshold
+    got = [f(ctypes.c_float(p)) for p in (-1.0, 0.0, 0.3, 0.34, 0.66, 0.67, 1.0, 2.0)]
+    assert got == [7.5, 7.5, 7.5, 5.0, 5.0, 2.5, 2.5, 2.5]
