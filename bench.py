@@ -84,6 +84,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--measure", default="maxprob",
+                    choices=["maxprob", "margin", "neg_entropy", "logit_gap"],
+                    help="confidence measure of the commit pass")
+    ap.add_argument("--early-gap", type=float, default=None,
+                    help="Prophet's early-commit threshold (one group per call)")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time complete multi-step decodes (pipelined active window) instead")
     ap.add_argument("--loop-blocks", type=int, default=8, help="blocks decoded per request")
@@ -205,8 +210,12 @@ def kernel_source_hash():
 
 def traffic_key(args):
     """Name of a workload's counter summary: the config, plus the block size
-    when one is chosen explicitly (the GQA config is measured per B)."""
-    return args.config if args.block_size is None else f"{args.config}_b{args.block_size}"
+    when one is chosen explicitly (the GQA config is measured per B) and the
+    confidence measure when it is not the maximum probability."""
+    key = args.config if args.block_size is None else f"{args.config}_b{args.block_size}"
+    if getattr(args, "measure", "maxprob") != "maxprob":
+        key += f"_{args.measure}"
+    return key
 
 
 def measured_traffic(config_name, call):
@@ -227,9 +236,10 @@ def measured_traffic(config_name, call):
 class Workload:
     """Rotating input sets of one configuration, resident on the GPU."""
 
-    def __init__(self, name, block_size, n_masks):
+    def __init__(self, name, block_size, n_masks, measure="maxprob", early_gap=None):
         import torch
         import workloads as W
+        self.measure, self.early_gap = measure, early_gap
         self.cfg = W.config(name, block_size=block_size)
         self.sh = sh = self.cfg["shape"]
         self.layers = self.cfg["layers"]
@@ -277,6 +287,8 @@ class Workload:
         self.conf = torch.empty(self.rows, dtype=torch.float32, device=dev)
         self.argmax = torch.empty(self.rows, dtype=torch.int32, device=dev)
         self.prefix_dev = torch.tensor(sh.prefix_len, dtype=torch.int32, device=dev)
+        self.early_gap_dev = (None if early_gap is None else
+                              torch.tensor([early_gap], dtype=torch.float32, device=dev))
         torch.cuda.synchronize()
 
     # --- the three calls ---------------------------------------------------
@@ -293,7 +305,8 @@ class Workload:
                                   self.phases, self.sh.block_size, self.tau, self.k_aggr,
                                   self.mask_token_id, conf_out=self.conf, argmax_out=self.argmax,
                                   n_committed=self.n_committed,
-                                  block_complete=self.block_complete, workspace=self.ws_commit)
+                                  block_complete=self.block_complete, workspace=self.ws_commit,
+                                  measure=self.measure, early_gap=self.early_gap_dev)
 
     def kv(self, r):
         import block_causal_attention_d2f_amd as d2f
@@ -623,7 +636,7 @@ def main():
         return
     K, Wu = args.steps, args.warmup
     n_masks = Wu + K + args.call_reps + 1
-    wl = Workload(args.config, args.block_size, n_masks)
+    wl = Workload(args.config, args.block_size, n_masks, args.measure, args.early_gap)
     sh = wl.sh
     use_graph = not args.no_graph
 
@@ -697,7 +710,8 @@ def main():
                    "n_win_blocks": (sh.n_win_blocks if sh.batch <= 4 else
                                     f"ragged, {sum(sh.n_win_blocks)} blocks"),
                    "layers": wl.layers, "vocab": wl.cfg["vocab"], "commit_rows": wl.rows,
-                   "tau": wl.tau, "input_sets": wl.n_sets,
+                   "tau": wl.tau, "measure": args.measure, "early_gap": args.early_gap,
+                   "input_sets": wl.n_sets,
                    "input_set_bytes": wl.set_bytes,
                    "launch": "hip-graph" if use_graph else "eager"},
         "step_bytes": step_bytes,
