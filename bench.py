@@ -89,6 +89,12 @@ def parse():
                     help="confidence measure of the commit pass")
     ap.add_argument("--early-gap", type=float, default=None,
                     help="Prophet's early-commit threshold (one group per call)")
+    ap.add_argument("--paged", action="store_true",
+                    help="keep K/V in a paged cache (one page per block; prefixes rounded down "
+                         "to whole blocks)")
+    ap.add_argument("--round-prefix", action="store_true",
+                    help="round prefixes down to whole blocks (the paged layout's workload, "
+                         "for a contiguous comparison)")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time complete multi-step decodes (pipelined active window) instead")
     ap.add_argument("--loop-blocks", type=int, default=8, help="blocks decoded per request")
@@ -215,6 +221,10 @@ def traffic_key(args):
     key = args.config if args.block_size is None else f"{args.config}_b{args.block_size}"
     if getattr(args, "measure", "maxprob") != "maxprob":
         key += f"_{args.measure}"
+    if getattr(args, "paged", False):
+        key += "_paged"
+    elif getattr(args, "round_prefix", False):
+        key += "_whole_blocks"
     return key
 
 
@@ -236,12 +246,21 @@ def measured_traffic(config_name, call):
 class Workload:
     """Rotating input sets of one configuration, resident on the GPU."""
 
-    def __init__(self, name, block_size, n_masks, measure="maxprob", early_gap=None):
+    def __init__(self, name, block_size, n_masks, measure="maxprob", early_gap=None,
+                 paged=False, round_prefix=False):
         import torch
         import workloads as W
-        self.measure, self.early_gap = measure, early_gap
+        self.measure, self.early_gap, self.paged = measure, early_gap, paged
         self.cfg = W.config(name, block_size=block_size)
-        self.sh = sh = self.cfg["shape"]
+        sh = self.cfg["shape"]
+        if paged or round_prefix:
+            B = sh.block_size
+            sh = W.make_shape(sh.batch, sh.n_heads_q, sh.n_heads_kv, sh.head_dim, B,
+                              [p // B * B for p in sh.prefix_len], sh.n_win_blocks,
+                              dtype=sh.dtype, max_win_blocks=sh.max_win_blocks,
+                              cache_capacity=sh.cache_capacity)
+            self.cfg["shape"] = sh
+        self.sh = sh
         self.layers = self.cfg["layers"]
         self.tau = self.cfg["taus"][0]
         self.k_aggr = self.cfg["k_aggr"]
@@ -261,6 +280,8 @@ class Workload:
             st = {n: torch.stack([x[n] for x in xs]) for n in xs[0]}
             ci = W.config_commit_inputs(self.cfg, device=dev, seed=r * 7919)
             st["logits"] = ci.logits
+            if paged:
+                self._to_pages(st)
             self.sets.append(st)
             del xs
         self.phases = ci.block_phase
@@ -276,7 +297,7 @@ class Workload:
         self.lse = torch.empty((self.layers,) + tuple(q0.shape[:3]), dtype=torch.float32,
                                device=dev)
         desc = d2f.make_desc(sh.batch, sh.n_heads_q, sh.n_heads_kv, sh.head_dim, sh.block_size,
-                             sh.max_win_blocks, sh.cache_capacity, q0.dtype)
+                             sh.max_win_blocks, sh.cache_capacity + sh.w_max, q0.dtype)
         need = d2f.d2f_block_attn_workspace_size(desc, sh.prefix_len, sh.n_win_blocks)
         self.ws_attn = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         need = d2f.d2f_confidence_commit_workspace_size(self.rows, self.cfg["vocab"])
@@ -291,10 +312,46 @@ class Workload:
                               torch.tensor([early_gap], dtype=torch.float32, device=dev))
         torch.cuda.synchronize()
 
+    def _to_pages(self, st):
+        """Move one input set's caches and windows into page pools (one pool
+        per layer, page ids shared by the layers, randomly numbered)."""
+        import torch
+        sh, B = self.sh, self.sh.block_size
+        L, nb, hkv, _, d = st["k_cache"].shape
+        if not hasattr(self, "page_table"):
+            n_cache = [p // B for p in sh.prefix_len]
+            self.n_pages = sum(n_cache) + sum(sh.n_win_blocks)
+            perm = torch.randperm(self.n_pages, generator=torch.Generator().manual_seed(1)).tolist()
+            ts = max(n_cache) + 1
+            pt = torch.full((nb, ts), -1, dtype=torch.int32)
+            wp = torch.full((nb, sh.max_win_blocks), -1, dtype=torch.int32)
+            for b in range(nb):
+                for i in range(n_cache[b]):
+                    pt[b, i] = perm.pop()
+                for k in range(sh.n_win_blocks[b]):
+                    wp[b, k] = perm.pop()
+            self.page_table, self.win_pages = pt.cuda(), wp.cuda()
+            self.pt_scratch, self.wp_scratch = self.page_table.clone(), self.win_pages.clone()
+        pt, wp = self.page_table.cpu(), self.win_pages.cpu()
+        for name, cname, wname in (("k_pages", "k_cache", "k_win"), ("v_pages", "v_cache", "v_win")):
+            pool = torch.empty((L, self.n_pages, hkv, B, d), dtype=st[cname].dtype, device="cuda")
+            for b in range(nb):
+                for i in range(sh.prefix_len[b] // B):
+                    pool[:, int(pt[b, i])] = st[cname][:, b, :, i * B:(i + 1) * B]
+                for k in range(sh.n_win_blocks[b]):
+                    pool[:, int(wp[b, k])] = st[wname][:, b, :, k * B:(k + 1) * B]
+            st[name] = pool
+            del st[cname], st[wname]
+
     # --- the three calls ---------------------------------------------------
     def attn(self, r, l):
         import block_causal_attention_d2f_amd as d2f
         s, sh = self.sets[r], self.sh
+        if self.paged:
+            d2f.d2f_block_attn_paged(s["q"][l], s["k_pages"][l], s["v_pages"][l], self.page_table,
+                                     self.win_pages, sh.prefix_len, sh.n_win_blocks,
+                                     out=self.out[l], lse=self.lse[l], workspace=self.ws_attn)
+            return
         d2f.d2f_block_attn(s["q"][l], s["k_cache"][l], s["v_cache"][l], s["k_win"][l],
                            s["v_win"][l], sh.prefix_len, sh.n_win_blocks, sh.block_size,
                            out=self.out[l], lse=self.lse[l], workspace=self.ws_attn)
@@ -312,6 +369,13 @@ class Workload:
         import block_causal_attention_d2f_amd as d2f
         s = self.sets[r]
         prefix = list(self.sh.prefix_len)  # the workload stays fixed from step to step
+        if self.paged:
+            # the persist moves page ids only: scratch tables keep the ones
+            # attention reads intact from step to step
+            d2f.d2f_kv_commit_paged(self.pt_scratch, self.wp_scratch, prefix, 0,
+                                    self.sh.block_size, n_heads_kv=self.sh.n_heads_kv,
+                                    head_dim=self.sh.head_dim, prefix_len_dev=self.prefix_dev)
+            return
         d2f.d2f_kv_commit(s["k_cache"], s["v_cache"], s["k_win"], s["v_win"], prefix, 0,
                           self.sh.block_size, prefix_len_dev=self.prefix_dev)
 
@@ -322,10 +386,16 @@ class Workload:
         self.commit(r, i)
         self.kv(r)
 
+    def kv_bytes(self):
+        """The append's compulsory bytes: K/V rows copied, or, paged, the
+        page ids moved."""
+        if self.paged:
+            return 4.0 * 2 * (self.sh.max_win_blocks + 1)
+        return kv_commit_bytes(self.sh, self.layers)
+
     def step_bytes(self):
         return (self.layers * attn_bytes(self.sh) +
-                commit_bytes(self.n_masked, self.rows, self.cfg["vocab"]) +
-                kv_commit_bytes(self.sh, self.layers))
+                commit_bytes(self.n_masked, self.rows, self.cfg["vocab"]) + self.kv_bytes())
 
 
 def capture(fn, use_graph):
@@ -636,7 +706,8 @@ def main():
         return
     K, Wu = args.steps, args.warmup
     n_masks = Wu + K + args.call_reps + 1
-    wl = Workload(args.config, args.block_size, n_masks, args.measure, args.early_gap)
+    wl = Workload(args.config, args.block_size, n_masks, args.measure, args.early_gap,
+                  args.paged, args.round_prefix)
     sh = wl.sh
     use_graph = not args.no_graph
 
@@ -656,7 +727,7 @@ def main():
     a_bytes = attn_bytes(sh)
     a_flops = attn_flops(sh)
     c_bytes = commit_bytes(wl.n_masked, wl.rows, wl.cfg["vocab"])
-    kv_b = kv_commit_bytes(sh, wl.layers)
+    kv_b = wl.kv_bytes()
     t_attn = calls["d2f_block_attn"] * 1e-3
     t_commit = calls["d2f_confidence_commit"] * 1e-3
     t_kv = calls["d2f_kv_commit"] * 1e-3
@@ -711,6 +782,8 @@ def main():
                                     f"ragged, {sum(sh.n_win_blocks)} blocks"),
                    "layers": wl.layers, "vocab": wl.cfg["vocab"], "commit_rows": wl.rows,
                    "tau": wl.tau, "measure": args.measure, "early_gap": args.early_gap,
+                   "kv_layout": "paged" if args.paged else "contiguous",
+                   "prefix_whole_blocks": bool(args.paged or args.round_prefix),
                    "input_sets": wl.n_sets,
                    "input_set_bytes": wl.set_bytes,
                    "launch": "hip-graph" if use_graph else "eager"},

@@ -7,10 +7,12 @@ thin ctypes binding.
     d2f_kv_commit           append a completed block to the KV cache
     Window                  the active-window schedule (host)
     d2f_decode_advance      one step's bookkeeping after the commit pass
+    d2f_block_attn_paged    attention over a paged cache (one page per block)
+    d2f_kv_commit_paged     persist a block by moving its page into the table
 """
 from ._binding import (AGGRESSIVE, COMMITTED, CONSERVATIVE, D2F_BF16, D2F_F32, EXPORTS,  # noqa: F401
                        LIB_PATH, MASKED, AttnDesc, D2FError, Window, d2f_block_attn,
-                       d2f_block_attn_workspace_size, d2f_confidence_commit,
+                       d2f_block_attn_paged, d2f_block_attn_workspace_size, d2f_confidence_commit,
                        d2f_confidence_commit_workspace_size, d2f_decode_advance,
-                       d2f_kv_commit, load, make_desc, prophet_threshold,
+                       d2f_kv_commit, d2f_kv_commit_paged, load, make_desc, prophet_threshold,
                        version)

@@ -28,6 +28,7 @@ CONSERVATIVE, AGGRESSIVE = 0, 1
 EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
            "d2f_confidence_commit_ex", "d2f_prophet_threshold",
+           "d2f_block_attn_paged", "d2f_kv_commit_paged",
            "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
            "d2f_status_string", "d2f_last_error", "d2f_version")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
@@ -91,6 +92,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                             _f32, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                             _vp, _sz, _vp]),
         "d2f_prophet_threshold": (_f32, [_f32]),
+        "d2f_block_attn_paged": (_i32, [pdesc, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _pi32, _pi32,
+                                        _vp, _vp, _vp, _sz, _vp]),
+        "d2f_kv_commit_paged": (_i32, [pdesc, _vp, _i32, _vp, _i32, _pi32, _vp, _vp]),
         "d2f_window_init": (_i32, [ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState)]),
         "d2f_window_after_commit": (_i32, [ctypes.POINTER(WindowParams),
                                            ctypes.POINTER(WindowState), _pi32, _pi32, _pi32]),
@@ -207,6 +211,60 @@ def d2f_kv_commit(k_cache, v_cache, k_win, v_win, prefix_len: list, request: int
     _check(load().d2f_kv_commit(ctypes.byref(desc), n_layers, _ptr(k_cache), _ptr(v_cache),
                                 kc0.numel(), _ptr(k_win), _ptr(v_win), kw0.numel(), int(request),
                                 int(block), pl, _ptr(prefix_len_dev), _stream(stream)))
+    prefix_len[request] = int(pl[request])
+    return prefix_len
+
+
+def d2f_block_attn_paged(q, k_pages, v_pages, page_table, win_pages, prefix_len, n_win_blocks,
+                         out=None, lse=None, want_lse=True, softmax_scale=0.0, workspace=None,
+                         stream=None):
+    """Block-causal attention over a paged cache (one layer; see d2f.h).
+
+    q [nb][Hq][Wmax][D] bf16; k_pages, v_pages [n_pages][Hkv][B][D] bf16 (one
+    page = one block); page_table int32 [nb][table_stride] and win_pages int32
+    [nb][Wmax / B] on the device; prefix_len (multiples of B), n_win_blocks:
+    host sequences.  Returns (out, lse)."""
+    nb, hq, wmax, d = q.shape
+    n_pages, hkv, bsz, d2 = k_pages.shape
+    if d2 != d or wmax % bsz:
+        raise ValueError("page and query shapes disagree")
+    for n, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _contig(n, t, q.dtype, q.device)
+    _contig("page_table", page_table, torch.int32, q.device)
+    _contig("win_pages", win_pages, torch.int32, q.device)
+    table_stride = page_table.shape[1] if page_table.dim() == 2 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    cap = table_stride * bsz + wmax
+    desc = make_desc(nb, hq, hkv, d, bsz, wmax // bsz, cap, q.dtype, softmax_scale)
+    need = d2f_block_attn_workspace_size(desc, prefix_len, n_win_blocks)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().d2f_block_attn_paged(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), n_pages, _ptr(page_table),
+        table_stride, _ptr(win_pages), _i32_array(prefix_len), _i32_array(n_win_blocks),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def d2f_kv_commit_paged(page_table, win_pages, prefix_len: list, request: int, block_size: int,
+                        n_heads_kv: int = 1, head_dim: int = 128, prefix_len_dev=None,
+                        stream=None):
+    """Persist request's oldest window block by moving its page into the page
+    table (no copy).  prefix_len (a Python list) is updated in place."""
+    nb, table_stride = page_table.shape
+    mw = win_pages.shape[1]
+    _contig("page_table", page_table, torch.int32, page_table.device)
+    _contig("win_pages", win_pages, torch.int32, page_table.device)
+    desc = make_desc(nb, n_heads_kv, n_heads_kv, head_dim, block_size, mw,
+                     table_stride * block_size, torch.bfloat16)
+    pl = _i32_array(prefix_len)
+    _check(load().d2f_kv_commit_paged(ctypes.byref(desc), _ptr(page_table), table_stride,
+                                      _ptr(win_pages), int(request), pl, _ptr(prefix_len_dev),
+                                      _stream(stream)))
     prefix_len[request] = int(pl[request])
     return prefix_len
 

@@ -235,6 +235,82 @@ size_t commit_workspace_bytes(int32_t n_rows, int32_t vocab) {
 }  // namespace
 }  // namespace d2f
 
+namespace d2f {
+namespace {
+
+// Page tables of a paged call (nullptr for contiguous caches).
+struct PagedRefs {
+  const int32_t* page_table;
+  const int32_t* win_pages;
+  int32_t table_stride;
+  int32_t n_pages;
+};
+
+// Plan and launch one attention call (arguments already validated).
+d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const void* k_cache,
+                           const void* v_cache, const void* k_win, const void* v_win,
+                           const int32_t* prefix_len_host, const int32_t* n_win_blocks_host,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t s, const PagedRefs* paged) {
+  std::vector<Launch> plan;
+  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace == nullptr ? (size_t)0 : workspace_bytes, need);
+  if (need > 0 && ((uintptr_t)workspace % 256) != 0)
+    return fail(D2F_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+  const float scale =
+      desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / std::sqrt((float)desc->head_dim);
+  for (const Launch& L : plan) {
+    AttnArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.kw = k_win;
+    a.vw = v_win;
+    a.out = out;
+    a.lse = lse;
+    a.ws_o = (float*)workspace;
+    a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * kQTile * desc->head_dim
+                          : nullptr;
+    a.cap = desc->cache_capacity;
+    a.qrows = L.qrows;
+    a.hq = desc->n_heads_q;
+    a.hkv = desc->n_heads_kv;
+    a.group = desc->n_heads_q / desc->n_heads_kv;
+    a.wmax = desc->max_win_blocks * desc->block_size;
+    a.bsz = desc->block_size;
+    a.n_req = (int)L.req.size();
+    a.n_units = L.n_units;
+    a.n_groups = L.n_groups;
+    a.remap = L.remap ? 1 : 0;
+    a.c2 = scale * 1.4426950408889634f;
+    if (paged != nullptr) {
+      a.page_table = paged->page_table;
+      a.win_pages = paged->win_pages;
+      a.table_stride = paged->table_stride;
+      a.n_pages = paged->n_pages;
+      int sh = 0;
+      while ((1 << sh) < desc->block_size) ++sh;
+      a.page_shift = sh;
+    }
+    for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
+    hipError_t e = desc->dtype == D2F_BF16
+                       ? launch_attn_bf16(a, desc->head_dim, paged != nullptr, s)
+                       : launch_attn_f32(a, desc->head_dim, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (L.any_split) {
+      e = launch_attn_merge(a, desc->head_dim, desc->dtype, s);
+      if (e != hipSuccess) return hip_fail(e, "split merge launch");
+    }
+  }
+  return D2F_OK;
+}
+
+}  // namespace
+}  // namespace d2f
+
 using namespace d2f;
 
 extern "C" {
@@ -268,6 +344,7 @@ d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
   return D2F_OK;
 }
 
+
 d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const void* k_cache,
                             const void* v_cache, const void* k_win, const void* v_win,
                             const int32_t* prefix_len_host, const int32_t* n_win_blocks_host,
@@ -292,52 +369,59 @@ d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const vo
       return fail(D2F_ERR_INVALID_ARG, "q/k/v/out buffers must be 16-byte aligned");
   if (((size_t)desc->head_dim * esz) % 16 != 0)
     return fail(D2F_ERR_UNSUPPORTED, "head_dim rows must be a multiple of 16 bytes");
+  return run_attention(desc, q, k_cache, v_cache, k_win, v_win, prefix_len_host,
+                       n_win_blocks_host, out, lse, workspace, workspace_bytes,
+                       (hipStream_t)stream, nullptr);
+}
 
-  std::vector<Launch> plan;
-  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
-                workspace == nullptr ? (size_t)0 : workspace_bytes, need);
-  if (need > 0 && ((uintptr_t)workspace % 256) != 0)
-    return fail(D2F_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-
-  const float scale =
-      desc->softmax_scale > 0.f ? desc->softmax_scale : 1.0f / std::sqrt((float)desc->head_dim);
-  hipStream_t s = (hipStream_t)stream;
-  for (const Launch& L : plan) {
-    AttnArgs a{};
-    a.q = q;
-    a.kc = k_cache;
-    a.vc = v_cache;
-    a.kw = k_win;
-    a.vw = v_win;
-    a.out = out;
-    a.lse = lse;
-    a.ws_o = (float*)workspace;
-    a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * kQTile * desc->head_dim
-                          : nullptr;
-    a.cap = desc->cache_capacity;
-    a.qrows = L.qrows;
-    a.hq = desc->n_heads_q;
-    a.hkv = desc->n_heads_kv;
-    a.group = desc->n_heads_q / desc->n_heads_kv;
-    a.wmax = desc->max_win_blocks * desc->block_size;
-    a.bsz = desc->block_size;
-    a.n_req = (int)L.req.size();
-    a.n_units = L.n_units;
-    a.n_groups = L.n_groups;
-    a.remap = L.remap ? 1 : 0;
-    a.c2 = scale * 1.4426950408889634f;
-    for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
-    hipError_t e = desc->dtype == D2F_BF16 ? launch_attn_bf16(a, desc->head_dim, s)
-                                           : launch_attn_f32(a, desc->head_dim, s);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    if (L.any_split) {
-      e = launch_attn_merge(a, desc->head_dim, desc->dtype, s);
-      if (e != hipSuccess) return hip_fail(e, "split merge launch");
-    }
+d2f_status_t d2f_block_attn_paged(const d2f_attn_desc_t* desc, const void* q,
+                                  const void* k_pages, const void* v_pages, int32_t n_pages,
+                                  const int32_t* page_table, int32_t table_stride,
+                                  const int32_t* win_pages, const int32_t* prefix_len_host,
+                                  const int32_t* n_win_blocks_host, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if (desc->dtype != D2F_BF16 || (desc->head_dim != 64 && desc->head_dim != 128))
+    return fail(D2F_ERR_UNSUPPORTED, "paged attention is built for bf16, head_dim 64 or 128");
+  const int B = desc->block_size;
+  if (B < 8 || (B & (B - 1)) != 0)
+    return fail(D2F_ERR_UNSUPPORTED, "paged attention needs a power-of-two block_size >= 8 "
+                "(got %d)", B);
+  if (desc->batch == 0) return D2F_OK;
+  if (prefix_len_host == nullptr || n_win_blocks_host == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "prefix_len_host / n_win_blocks_host is NULL");
+  if (n_pages < 1 || table_stride < 0)
+    return fail(D2F_ERR_INVALID_ARG, "n_pages %d / table_stride %d out of range", n_pages,
+                table_stride);
+  bool any_prefix = false, any_win = false;
+  for (int b = 0; b < desc->batch; ++b) {
+    const int P = prefix_len_host[b], n = n_win_blocks_host[b];
+    if (P < 0 || P % B != 0)
+      return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d is not a whole number of blocks", b,
+                  P);
+    if (n < 0 || n > desc->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b, n,
+                  desc->max_win_blocks);
+    if (P / B > table_stride)
+      return fail(D2F_ERR_CAPACITY, "request %d: %d cached blocks, table holds %d", b, P / B,
+                  table_stride);
+    any_prefix |= P > 0;
+    any_win |= n > 0;
   }
-  return D2F_OK;
+  if (q == nullptr || out == nullptr || k_pages == nullptr || v_pages == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "q, out and the page pools must not be NULL");
+  if ((any_prefix && page_table == nullptr) || (any_win && win_pages == nullptr))
+    return fail(D2F_ERR_INVALID_ARG, "page table or window pages are NULL");
+  for (const void* p : {q, k_pages, v_pages, (const void*)out})
+    if (((uintptr_t)p % 16) != 0)
+      return fail(D2F_ERR_INVALID_ARG, "q/pages/out buffers must be 16-byte aligned");
+  if ((unsigned long long)n_pages * desc->n_heads_kv * B * desc->head_dim * 2 >= (1ULL << 62))
+    return fail(D2F_ERR_INVALID_ARG, "page pool too large");
+  const PagedRefs refs{page_table, win_pages, table_stride, n_pages};
+  return run_attention(desc, q, k_pages, v_pages, nullptr, nullptr, prefix_len_host,
+                       n_win_blocks_host, out, lse, workspace, workspace_bytes,
+                       (hipStream_t)stream, &refs);
 }
 
 d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache,
@@ -388,6 +472,31 @@ d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* 
   hipError_t e = launch_kv_commit(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv commit launch");
   prefix_len_host[request] = P + desc->block_size;
+  return D2F_OK;
+}
+
+d2f_status_t d2f_kv_commit_paged(const d2f_attn_desc_t* desc, int32_t* page_table,
+                                 int32_t table_stride, int32_t* win_pages, int32_t request,
+                                 int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                                 d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if (request < 0 || request >= desc->batch)
+    return fail(D2F_ERR_INVALID_ARG, "request %d outside [0, %d)", request, desc->batch);
+  if (page_table == nullptr || win_pages == nullptr || prefix_len_host == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "page table, window pages or prefix lengths are NULL");
+  const int B = desc->block_size;
+  const int32_t P = prefix_len_host[request];
+  if (P < 0 || P % B != 0)
+    return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d is not a whole number of blocks",
+                request, P);
+  if (P / B >= table_stride)
+    return fail(D2F_ERR_CAPACITY, "page table full: %d blocks, %d slots", P / B, table_stride);
+  hipError_t e = launch_kv_commit_paged(page_table, win_pages, prefix_len_dev, request,
+                                        table_stride, desc->max_win_blocks, P / B, P + B,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "paged kv commit launch");
+  prefix_len_host[request] = P + B;
   return D2F_OK;
 }
 

@@ -111,7 +111,10 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 // QB: 16-row query blocks per wave (2: 64 query rows per unit, 1: 32).
-template <int D, int QB>
+// PAGED: 0 contiguous K/V; otherwise rows are found through the page tables
+// (see AttnArgs): 1 for 8-row pages, 2 for pages of 16 rows or more, where the
+// 16 rows a wave loads of a tile always share one page.
+template <int D, int QB, int PAGED>
 __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;                // LDS row bytes
   constexpr int KSTEPS = D / 32;           // MFMA k-steps over head_dim
@@ -172,7 +175,60 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     vb = (const char*)((in_cache ? vc : vw) + o);
   };
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Paged rows: a 1 KB block holds RPB consecutive rows starting at a
+  // multiple of RPB, and a page holds bsz rows with bsz a multiple of RPB,
+  // so the rows of one direct load lie in one page and its base stays
+  // uniform (a block wholly past a partial tile's end re-reads the tile's
+  // last row).  The page ids of the next tile are fetched while the current
+  // one is issued: lane j of a wave holds the page of its block j and that
+  // page's first row relative to the tile, and the tile barrier's wait for
+  // all loads covers them, so no issue waits on a table read.  Page ids are
+  // clamped to the pool, so a bad table entry reads the wrong rows, never
+  // outside the pool.
+  static_assert(RPB * LPW == 16, "a wave loads 16 rows of a tile");
+  const size_t page_elems = (size_t)a.hkv * B * D;
+  const int pshift = a.page_shift;  // bsz = 1 << pshift
+  int pg_page = 0, pg_row0 = 0;  // lane j < LPW: block j of the tile issued next
+  auto fetch_pages = [&](int t) {
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
+    const bool in_cache = t < nct;
+    const int r0 = in_cache ? lo : lo - P;  // first row's index in the cache or the window
+    const int32_t* table = in_cache ? a.page_table + (size_t)rb * a.table_stride
+                                    : a.win_pages + (size_t)rb * (a.wmax / B);
+    const int j = (PAGED == 1 && lane < LPW) ? lane : 0;
+    const int key0 = r0 + min(RPB * (LPW * wave_u + j), nv - 1);
+    const int pi = key0 >> pshift;
+    pg_page = min(max(table[pi], 0), a.n_pages - 1);
+    pg_row0 = (pi << pshift) - r0;
+  };
+  auto issue_paged = [&](auto J, int t) {
+    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, 2 * TILE>();
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
+    int page = __builtin_amdgcn_readfirstlane(pg_page);
+    int row0 = __builtin_amdgcn_readfirstlane(pg_row0);
+    size_t pbase = ((size_t)page * page_elems + (size_t)kvh * B * D) * sizeof(__bf16);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = LPW * wave_u + j;
+      if (PAGED == 1 && j > 0) {
+        page = __builtin_amdgcn_readlane(pg_page, j);
+        row0 = __builtin_amdgcn_readlane(pg_row0, j);
+        pbase = ((size_t)page * page_elems + (size_t)kvh * B * D) * sizeof(__bf16);
+      }
+      const int row = RPB * blk + lane / CPR;
+      const int off = (min(row, nv - 1) - row0) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
+      load_lds16((const char*)a.kc + pbase, off, sb + blk * 1024);
+      load_lds16((const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
+    }
+    fetch_pages(min(t + 1, t_hi - 1));
+  };
   auto issue = [&](auto J, int t) {
+    if constexpr (PAGED != 0) {
+      issue_paged(J, t);
+      return;
+    }
     const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, 2 * TILE>();
     const char *kb, *vb;
     int nv;
@@ -190,6 +246,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // The first tile is requested before the queries are loaded, so that its
   // latency and theirs overlap.  Tiles past the last re-read the last tile.
   auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
+  if (PAGED != 0 && n_tiles > 0) fetch_pages(tile_at(0));
   if (n_tiles > 0) issue(ic<0>{}, tile_at(0));
 
   // This lane's two queries (MFMA column lc of the wave's two row blocks).
@@ -429,26 +486,34 @@ int attn_bf16_wgs_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2>, kAttnThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2, 0>,
+                                                     kAttnThreads, 0);
   else if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2>, kAttnThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2, 0>,
+                                                     kAttnThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
+template <int PAGED>
+hipError_t launch_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.n_units), block(kAttnThreads);
   const bool narrow = a.qrows == 32;
   if (head_dim == 128 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, PAGED>), grid, block, 0, s, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, PAGED>), grid, block, 0, s, a);
   else if (head_dim == 64 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, PAGED>), grid, block, 0, s, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, PAGED>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {
+  if (!paged) return launch_bf16<0>(a, head_dim, s);
+  return a.bsz >= 16 ? launch_bf16<2>(a, head_dim, s) : launch_bf16<1>(a, head_dim, s);
 }
 
 }  // namespace d2f

@@ -46,6 +46,14 @@ struct AttnArgs {
   int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
   int32_t qrows;  // query rows per unit: kQTile, or 32 (bf16, narrow windows)
   float c2;       // softmax scale * log2(e)
+  // Paged K/V (bf16 only): kc/vc are page pools [n_pages][hkv][bsz][D];
+  // cache key p of request b is row p % bsz of page page_table[b][p / bsz],
+  // window key w is row w % bsz of page win_pages[b][w / bsz].
+  const int32_t* page_table;  // [batch][table_stride]
+  const int32_t* win_pages;   // [batch][wmax / bsz]
+  int32_t table_stride;
+  int32_t n_pages;
+  int32_t page_shift;  // bsz = 1 << page_shift (paged only)
   ReqInfo req[kMaxReqPerLaunch];
 };
 
@@ -108,7 +116,7 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 }
 
 // Launchers (each returns hipSuccess or the launch error).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool paged, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
 // Attention workgroups that fit on one CU at once (0 if unknown).
 int attn_bf16_wgs_per_cu(int head_dim);
@@ -159,6 +167,8 @@ struct KvArgs {
   int32_t* prefix_dev;
 };
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t s);
+hipError_t launch_kv_commit_paged(int32_t* table, int32_t* win, int32_t* prefix_dev, int b,
+                                  int ts, int mw, int slot, int new_prefix, hipStream_t s);
 
 // One decoding step's bookkeeping after the commit pass, for up to
 // kMaxReqPerLaunch requests (decode.hip).

@@ -40,7 +40,30 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(const KvArgs a) {
   if (idx == 0 && threadIdx.x == 0 && a.prefix_dev != nullptr) a.prefix_dev[a.request] = a.new_prefix;
 }
 
+// Paged persist: the page of the oldest window block joins the request's
+// page table at slot `slot` and the window's page list moves up by one (its
+// last entry becomes -1, to be filled by the caller when a block is
+// appended).  One thread: a handful of integers.
+__global__ __launch_bounds__(64) void kv_commit_paged_kernel(int32_t* table, int32_t* win,
+                                                             int32_t* prefix_dev, int b, int ts,
+                                                             int mw, int slot, int new_prefix) {
+  if (threadIdx.x != 0) return;
+  int32_t* w = win + (size_t)b * mw;
+  const int32_t first = w[0];
+  for (int k = 0; k + 1 < mw; ++k) w[k] = w[k + 1];
+  w[mw - 1] = -1;
+  table[(size_t)b * ts + slot] = first;
+  if (prefix_dev != nullptr) prefix_dev[b] = new_prefix;
+}
+
 }  // namespace
+
+hipError_t launch_kv_commit_paged(int32_t* table, int32_t* win, int32_t* prefix_dev, int b,
+                                  int ts, int mw, int slot, int new_prefix, hipStream_t s) {
+  hipLaunchKernelGGL(kv_commit_paged_kernel, dim3(1), dim3(64), 0, s, table, win, prefix_dev, b,
+                     ts, mw, slot, new_prefix);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t s) {
   const size_t esz = (size_t)a.esize;

@@ -157,6 +157,55 @@ d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* 
                            int32_t block, int32_t* prefix_len_host, int32_t* prefix_len_dev,
                            d2f_stream_t stream);
 
+/* ---- Paged KV cache: block completion as the persist signal ----
+ *
+ * [D2F-wiki] section "운영 관점" (KV cache management): completed blocks are
+ * cached permanently; a paged cache (as in PagedAttention) can be used with
+ * the completion of a block as the signal that makes its entries permanent.
+ * [D2F-wiki] section "블록 단위 인과 어텐션": a completed block's K/V no
+ * longer change.
+ *
+ * A page holds the K (or V) rows of one D2F block for every KV head of one
+ * layer: pools k_pages, v_pages are [n_pages][n_heads_kv][block_size][head_dim]
+ * (dtype elements; one pool per layer, page ids shared by all layers).
+ * Request b's cached keys are the pages page_table[b][0 .. P/B) in order
+ * (page_table: device int32 [batch][table_stride]); its window block k is
+ * page win_pages[b][k] (device int32 [batch][max_win_blocks]).  The model
+ * writes a window block's K/V into that block's page, so when the oldest
+ * window block completes, d2f_kv_commit_paged moves its page id into the page
+ * table: nothing is copied.  Pages are owned and handed out by the caller.
+ *
+ * d2f_block_attn_paged computes exactly what d2f_block_attn computes for the
+ * same keys (same kernels and work plan; only the K/V addressing differs), with
+ * q, out, lse laid out as there.  Requirements: bf16, head_dim 64 or 128,
+ * block_size a power of two >= 8 (D2F_ERR_UNSUPPORTED otherwise); every
+ * prefix_len_host[b] a multiple of block_size (D2F_ERR_INVALID_ARG; the
+ * cache holds whole blocks) with P/B <= table_stride (D2F_ERR_CAPACITY);
+ * 0 <= n_win_blocks_host[b] <= max_win_blocks.  desc->cache_capacity is not
+ * used.  The workspace is the one d2f_block_attn_workspace_size gives for the
+ * same lengths (with a desc whose cache_capacity covers P + W).  Page ids
+ * read outside [0, n_pages) are clamped into the pool (the results are then
+ * meaningless, but nothing outside the pool is read).
+ */
+d2f_status_t d2f_block_attn_paged(const d2f_attn_desc_t* desc, const void* q,
+                                  const void* k_pages, const void* v_pages, int32_t n_pages,
+                                  const int32_t* page_table, int32_t table_stride,
+                                  const int32_t* win_pages, const int32_t* prefix_len_host,
+                                  const int32_t* n_win_blocks_host, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, d2f_stream_t stream);
+
+/* Persist the oldest window block of `request` in the paged cache: on
+ * `stream`, page_table[request][P/B] = win_pages[request][0], the window's page
+ * list moves up by one (its last entry becomes -1; the caller puts a free page
+ * there before a block is appended), and prefix_len_dev[request] = P + B when
+ * prefix_len_dev is not NULL; prefix_len_host[request] += B on return.
+ * Errors: D2F_ERR_INVALID_ARG (request out of range, P not a multiple of B,
+ * NULL pointers), D2F_ERR_CAPACITY (P/B >= table_stride), D2F_ERR_HIP. */
+d2f_status_t d2f_kv_commit_paged(const d2f_attn_desc_t* desc, int32_t* page_table,
+                                 int32_t table_stride, int32_t* win_pages, int32_t request,
+                                 int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                                 d2f_stream_t stream);
+
 /* Bytes of device workspace d2f_confidence_commit and d2f_confidence_commit_ex
  * need (16-byte aligned; its contents need no initialisation). */
 d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,

@@ -16,7 +16,7 @@ Sources (cited by page title and section; the short names are used below):
 * [dLLM-survey] "확산 언어 모델(Diffusion LLM)이란 무엇인가", discuss.pytorch.kr.
 
 Modules:
-  attention  block-causal window attention over a frozen cache
+  attention  block-causal window attention over a frozen cache (contiguous or paged)
   commit     per-position confidence/argmax and the block commit rule
   kv_cache   appending a completed block to the cache
   window     the active-window schedule of pipelined decoding

@@ -97,3 +97,42 @@ def block_attn(q, k_cache, v_cache, k_win, v_win, prefix_len, n_win_blocks, bloc
         out[b, h, :W] = o
         lse[b, h, :W] = l
     return out, lse
+
+
+def gather_pages(pages, table_row, n_blocks):
+    """The rows of the first n_blocks pages listed in table_row, in order:
+    pages [n_pages][Hkv][B][D] -> [Hkv][n_blocks * B][D] (float64)."""
+    pages = as_f64(pages)
+    hkv, B, d = pages.shape[1:]
+    if n_blocks == 0:
+        return np.zeros((hkv, 0, d))
+    ids = [int(i) for i in np.asarray(table_row)[:n_blocks]]
+    return np.concatenate([pages[i] for i in ids], axis=1)
+
+
+def block_attn_paged(q, k_pages, v_pages, page_table, win_pages, prefix_len, n_win_blocks,
+                     block_size, scale=None, pairs=None):
+    """Window attention over a paged cache: request b's cache is the pages
+    page_table[b][0 .. P/B) and its window block k is page win_pages[b][k]
+    ([D2F-wiki] section "운영 관점", KV cache management: completed blocks kept
+    in a paged cache).  The keys are gathered into the contiguous layout and
+    block_attn applies the definition; rows past the window are NaN."""
+    q = as_f64(q)
+    nb, hq, wmax, d = q.shape
+    B = int(block_size)
+    kp, vp = as_f64(k_pages), as_f64(v_pages)
+    hkv = kp.shape[1]
+    cap = max([int(p) for p in prefix_len] + [0]) + wmax
+    kc = np.zeros((nb, hkv, max(cap, 1), d))
+    vc = np.zeros_like(kc)
+    kw = np.zeros((nb, hkv, wmax, d))
+    vw = np.zeros_like(kw)
+    pt, wp = np.asarray(page_table), np.asarray(win_pages)
+    for b in range(nb):
+        P, n = int(prefix_len[b]), int(n_win_blocks[b])
+        assert P % B == 0
+        kc[b, :, :P] = gather_pages(kp, pt[b] if P else [], P // B)
+        vc[b, :, :P] = gather_pages(vp, pt[b] if P else [], P // B)
+        kw[b, :, :n * B] = gather_pages(kp, wp[b] if n else [], n)
+        vw[b, :, :n * B] = gather_pages(vp, wp[b] if n else [], n)
+    return block_attn(q, kc, vc, kw, vw, prefix_len, n_win_blocks, B, scale=scale, pairs=pairs)

@@ -36,3 +36,23 @@ def drop_oldest_block(x, request, block_size):
     y[b, :, :-B] = np.asarray(x)[b, :, B:]
     y[b, :, -B:] = np.nan
     return y
+
+
+def kv_commit_paged(page_table, win_pages, prefix_len, request, block_size):
+    """Paged persist ([D2F-wiki] section "운영 관점", KV cache management: block
+    completion is the signal that makes its entries permanent): the page of
+    request's oldest window block becomes cache page P / B; the window's page
+    list moves up by one and its last entry becomes -1; P grows by B.
+    Returns (page_table', win_pages', prefix_len')."""
+    pt = np.array(page_table, copy=True)
+    wp = np.array(win_pages, copy=True)
+    p = [int(x) for x in prefix_len]
+    b, B = int(request), int(block_size)
+    P = p[b]
+    if P % B or P // B >= pt.shape[1]:
+        raise ValueError("prefix not whole blocks, or page table full")
+    pt[b, P // B] = wp[b, 0]
+    wp[b, :-1] = np.asarray(win_pages)[b, 1:]
+    wp[b, -1] = -1
+    p[b] = P + B
+    return pt, wp, p

@@ -202,3 +202,32 @@ def test_prophet_threshold_steps(lib):
     f = lib.d2f_prophet_threshold
     got = [f(ctypes.c_float(p)) for p in (-1.0, 0.0, 0.3, 0.34, 0.66, 0.67, 1.0, 2.0)]
     assert got == [7.5, 7.5, 7.5, 5.0, 5.0, 2.5, 2.5, 2.5]
+
+
+def paged(lib, d, prefix, nwin, table_stride=8, n_pages=16, pt=FAKE, wp=FAKE):
+    n = max(1, len(prefix))
+    return lib.d2f_block_attn_paged(ctypes.byref(d), FAKE, FAKE, FAKE, n_pages, pt, table_stride,
+                                    wp, (ctypes.c_int32 * n)(*prefix), (ctypes.c_int32 * n)(*nwin),
+                                    FAKE, None, FAKE, 1 << 30, None)
+
+
+def test_paged_attention_errors(lib):
+    assert paged(lib, desc(dtype=B.D2F_F32), [16], [1]) == UNSUPPORTED     # bf16 only
+    assert paged(lib, desc(block_size=12), [24], [1]) == UNSUPPORTED       # not a power of two
+    assert paged(lib, desc(block_size=4), [8], [1]) == UNSUPPORTED         # below 8
+    assert paged(lib, desc(), [24], [1]) == INVALID                        # not whole blocks
+    assert b"whole number of blocks" in lib.d2f_last_error()
+    assert paged(lib, desc(), [160], [1], table_stride=8) == CAPACITY      # 10 blocks > 8 slots
+    assert paged(lib, desc(), [16], [4]) == INVALID                        # > max_win_blocks
+    assert paged(lib, desc(), [16], [1], pt=None) == INVALID               # table missing
+    assert paged(lib, desc(), [16], [1], n_pages=0) == INVALID
+    assert paged(lib, desc(batch=0), [], []) == OK
+
+
+def test_paged_persist_errors(lib):
+    d = desc(batch=2)
+    pl = (ctypes.c_int32 * 2)(16, 24)
+    assert lib.d2f_kv_commit_paged(ctypes.byref(d), FAKE, 4, FAKE, 1, pl, None, None) == INVALID
+    assert lib.d2f_kv_commit_paged(ctypes.byref(d), FAKE, 1, FAKE, 0, pl, None, None) == CAPACITY
+    assert lib.d2f_kv_commit_paged(ctypes.byref(d), FAKE, 4, FAKE, 2, pl, None, None) == INVALID
+    assert list(pl) == [16, 24]
