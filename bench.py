@@ -521,6 +521,7 @@ class DecodeLoop:
         import torch
         import workloads as W
         import block_causal_attention_d2f_amd as d2f
+        self.paged = args.paged
         self.cfg = cfg = W.config("cfg3")
         sh = cfg["shape"]
         self.nb, self.hq, self.hkv, self.d, self.B = (sh.batch, sh.n_heads_q, sh.n_heads_kv,
@@ -530,6 +531,8 @@ class DecodeLoop:
         self.tau, self.k_aggr = cfg["taus"][0], cfg["k_aggr"]
         self.tau_add, self.tau_act = args.tau_add, args.tau_act
         self.prompt = list(sh.prefix_len)
+        if self.paged:  # the paged cache holds whole blocks
+            self.prompt = [p // self.B * self.B for p in self.prompt]
         self.cap = max(self.prompt) + self.total * self.B
         self.wmax = self.mw * self.B
         self.mask_id = self.vocab
@@ -540,11 +543,26 @@ class DecodeLoop:
         def randn(*shape):
             return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(bf)
         L, nb, hq, hkv, d = self.L, self.nb, self.hq, self.hkv, self.d
-        self.kc = torch.empty((L, nb, hkv, self.cap, d), dtype=bf, device=dev)
-        self.vc = torch.empty_like(self.kc)
-        for l in range(L):  # layer by layer keeps the fp32 staging small
-            self.kc[l] = randn(nb, hkv, self.cap, d)
-            self.vc[l] = randn(nb, hkv, self.cap, d)
+        if self.paged:
+            # pages for the prompts, the first block of each window and one
+            # per later block; ids in random order
+            self.n_pages = sum(p // self.B for p in self.prompt) + nb * (self.total + 1)
+            self.kc = torch.empty((L, self.n_pages, hkv, self.B, d), dtype=bf, device=dev)
+            self.vc = torch.empty_like(self.kc)
+            for l in range(L):
+                self.kc[l] = randn(self.n_pages, hkv, self.B, d)
+                self.vc[l] = randn(self.n_pages, hkv, self.B, d)
+            self.page_order = torch.randperm(
+                self.n_pages, generator=torch.Generator().manual_seed(5)).tolist()
+            self.table_stride = max(self.prompt) // self.B + self.total
+            self.page_table = torch.empty((nb, self.table_stride), dtype=torch.int32, device=dev)
+            self.win_pages = torch.empty((nb, self.mw), dtype=torch.int32, device=dev)
+        else:
+            self.kc = torch.empty((L, nb, hkv, self.cap, d), dtype=bf, device=dev)
+            self.vc = torch.empty_like(self.kc)
+            for l in range(L):  # layer by layer keeps the fp32 staging small
+                self.kc[l] = randn(nb, hkv, self.cap, d)
+                self.vc[l] = randn(nb, hkv, self.cap, d)
         self.q = randn(L, nb, hq, self.wmax, d)
         self.kw = randn(L, nb, hkv, self.wmax, d)
         self.vw = randn(L, nb, hkv, self.wmax, d)
@@ -582,6 +600,19 @@ class DecodeLoop:
         self.prefix_dev.copy_(torch.tensor(self.P, dtype=torch.int32))
         self.wins = [d2f.Window(self.B, self.mw, self.total, self.tau_add, self.tau_act)
                      for _ in range(self.nb)]
+        if self.paged:
+            import numpy as np
+            order = list(self.page_order)
+            pt = np.full((self.nb, self.table_stride), -1, dtype=np.int32)
+            wp = np.full((self.nb, self.mw), -1, dtype=np.int32)
+            for b in range(self.nb):
+                n = self.prompt[b] // self.B
+                pt[b, :n] = order[len(order) - n:][::-1]
+                del order[len(order) - n:]
+                wp[b, 0] = order.pop()
+            self.page_table.copy_(torch.from_numpy(pt))
+            self.win_pages.copy_(torch.from_numpy(wp))
+            self.free = order
         torch.cuda.synchronize()
 
     def step(self, i, ev=None):
@@ -590,24 +621,40 @@ class DecodeLoop:
         rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
         rec(0)
         for l in range(self.L):
-            d2f.d2f_block_attn(self.q[l], self.kc[l], self.vc[l], self.kw[l], self.vw[l], self.P,
-                               nwin, self.B, out=self.out, lse=self.lse, workspace=self.ws_attn)
+            if self.paged:   # the window's K/V are the resident random pages
+                d2f.d2f_block_attn_paged(self.q[l], self.kc[l], self.vc[l], self.page_table,
+                                         self.win_pages, self.P, nwin, out=self.out,
+                                         lse=self.lse, workspace=self.ws_attn)
+            else:
+                d2f.d2f_block_attn(self.q[l], self.kc[l], self.vc[l], self.kw[l], self.vw[l],
+                                   self.P, nwin, self.B, out=self.out, lse=self.lse,
+                                   workspace=self.ws_attn)
         rec(1)
         d2f.d2f_confidence_commit(self.pool[i % len(self.pool)], self.ms, self.tk, self.ph,
                                   self.B, self.tau, self.k_aggr, self.mask_id, n_committed=self.ncd,
                                   block_complete=self.bcd, workspace=self.ws_commit,
                                   want_conf=False)
         rec(2)
-        d2f.d2f_decode_advance(self.kc, self.vc, self.kw, self.vw, self.wins, self.P, self.ncd,
-                               self.ms, self.tk, self.ph, self.outt, self.mask_id,
-                               prefix_len_dev=self.prefix_dev)
+        if self.paged:
+            new = [self.free.pop() for _ in range(self.nb)]
+            _, app = d2f.d2f_decode_advance_paged(
+                self.page_table, self.win_pages, new, self.wins, self.P, self.ncd, self.ms,
+                self.tk, self.ph, self.outt, self.mask_id, n_heads_kv=self.hkv, head_dim=self.d,
+                prefix_len_dev=self.prefix_dev)
+            self.free.extend(pg for pg, a in zip(new, app) if not a)
+        else:
+            d2f.d2f_decode_advance(self.kc, self.vc, self.kw, self.vw, self.wins, self.P,
+                                   self.ncd, self.ms, self.tk, self.ph, self.outt, self.mask_id,
+                                   prefix_len_dev=self.prefix_dev)
         rec(3)
         return nwin
 
     def decode(self, events=False):
-        """One complete decode; returns the per-step windows and events."""
+        """One complete decode; returns the per-step windows and events, and
+        the wall time of the steps (the set-up of the decode is not timed)."""
         import torch
         self.reset()
+        t0 = time.perf_counter()
         steps = []
         while not all(w.done for w in self.wins):
             if len(steps) > 100 * self.total:
@@ -617,6 +664,7 @@ class DecodeLoop:
             nwin = self.step(len(steps), ev)
             steps.append((prefix, nwin, ev))
         torch.cuda.synchronize()
+        self.wall = time.perf_counter() - t0
         return steps
 
 
@@ -628,10 +676,8 @@ def decode_loop_main(args):
     outs = lp.outt.clone()
     walls, n_steps = [], []
     for _ in range(args.loop_reps):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         st = lp.decode()
-        walls.append(time.perf_counter() - t0)
+        walls.append(lp.wall)
         n_steps.append(len(st))
         assert torch.equal(lp.outt, outs), "decodes of the same inputs differ"
     assert (outs >= 0).all() and (outs != lp.mask_id).all(), "undecoded positions left"
@@ -670,7 +716,8 @@ def decode_loop_main(args):
                    "max_window_blocks": lp.mw, "prompt_len": f"U(256, 4096), mean "
                    f"{sum(lp.prompt) / lp.nb:.0f}", "vocab": lp.vocab, "tau": lp.tau,
                    "k_aggr": lp.k_aggr, "tau_add": lp.tau_add, "tau_act": lp.tau_act,
-                   "timed_decodes": args.loop_reps, "launch": "eager"},
+                   "timed_decodes": args.loop_reps, "launch": "eager",
+                   "kv_layout": "paged" if lp.paged else "contiguous"},
         "tokens_per_decode": tokens,
         "tokens_per_step": round(tokens / steps, 2),
         "wall_s_per_decode": round(wall, 5),

@@ -14,5 +14,6 @@ from ._binding import (AGGRESSIVE, COMMITTED, CONSERVATIVE, D2F_BF16, D2F_F32, E
                        LIB_PATH, MASKED, AttnDesc, D2FError, Window, d2f_block_attn,
                        d2f_block_attn_paged, d2f_block_attn_workspace_size, d2f_confidence_commit,
                        d2f_confidence_commit_workspace_size, d2f_decode_advance,
+                       d2f_decode_advance_paged,
                        d2f_kv_commit, d2f_kv_commit_paged, load, make_desc, prophet_threshold,
                        version)

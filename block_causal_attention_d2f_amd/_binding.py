@@ -28,7 +28,7 @@ CONSERVATIVE, AGGRESSIVE = 0, 1
 EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
            "d2f_confidence_commit_ex", "d2f_prophet_threshold",
-           "d2f_block_attn_paged", "d2f_kv_commit_paged",
+           "d2f_block_attn_paged", "d2f_kv_commit_paged", "d2f_decode_advance_paged",
            "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
            "d2f_status_string", "d2f_last_error", "d2f_version")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
@@ -95,6 +95,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "d2f_block_attn_paged": (_i32, [pdesc, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _pi32, _pi32,
                                         _vp, _vp, _vp, _sz, _vp]),
         "d2f_kv_commit_paged": (_i32, [pdesc, _vp, _i32, _vp, _i32, _pi32, _vp, _vp]),
+        "d2f_decode_advance_paged": (_i32, [pdesc, _vp, _i32, _vp, _pi32,
+                                            ctypes.POINTER(WindowParams),
+                                            ctypes.POINTER(WindowState), _pi32, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _i32, _pi32, _pi32, _vp]),
         "d2f_window_init": (_i32, [ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState)]),
         "d2f_window_after_commit": (_i32, [ctypes.POINTER(WindowParams),
                                            ctypes.POINTER(WindowState), _pi32, _pi32, _pi32]),
@@ -183,14 +187,25 @@ def d2f_block_attn(q, k_cache, v_cache, k_win, v_win, prefix_len, n_win_blocks, 
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     pl, nw = _i32_array(prefix_len), _i32_array(n_win_blocks)
-    need = d2f_block_attn_workspace_size(desc, prefix_len, n_win_blocks)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().d2f_block_attn(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(k_win), _ptr(v_win), pl, nw, _ptr(out), _ptr(lse),
-                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+    def call(ws):
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        return load().d2f_block_attn(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_win), _ptr(v_win), pl, nw, _ptr(out), _ptr(lse),
+                                     _ptr(ws), nbytes, _stream(stream))
+    _call_with_workspace(call, workspace, lambda: d2f_block_attn_workspace_size(
+        desc, prefix_len, n_win_blocks), q.device)
     return out, lse
+
+
+def _call_with_workspace(call, workspace, size, device):
+    """Run call(workspace); only if the library reports the workspace too
+    small (which it checks before launching anything), size it and run again
+    -- so the work plan is made once per call in the common case."""
+    st = call(workspace)
+    if st == 4:  # D2F_ERR_WORKSPACE
+        st = call(torch.empty(max(size(), 256), dtype=torch.uint8, device=device))
+    _check(st)
 
 
 def d2f_kv_commit(k_cache, v_cache, k_win, v_win, prefix_len: list, request: int,
@@ -239,14 +254,16 @@ def d2f_block_attn_paged(q, k_pages, v_pages, page_table, win_pages, prefix_len,
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     cap = table_stride * bsz + wmax
     desc = make_desc(nb, hq, hkv, d, bsz, wmax // bsz, cap, q.dtype, softmax_scale)
-    need = d2f_block_attn_workspace_size(desc, prefix_len, n_win_blocks)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().d2f_block_attn_paged(
-        ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), n_pages, _ptr(page_table),
-        table_stride, _ptr(win_pages), _i32_array(prefix_len), _i32_array(n_win_blocks),
-        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    pl, nw = _i32_array(prefix_len), _i32_array(n_win_blocks)
+
+    def call(ws):
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        return load().d2f_block_attn_paged(
+            ctypes.byref(desc), _ptr(q), _ptr(k_pages), _ptr(v_pages), n_pages, _ptr(page_table),
+            table_stride, _ptr(win_pages), pl, nw, _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+            _stream(stream))
+    _call_with_workspace(call, workspace, lambda: d2f_block_attn_workspace_size(
+        desc, prefix_len, n_win_blocks), q.device)
     return out, lse
 
 
@@ -449,6 +466,50 @@ def d2f_decode_advance(k_cache, v_cache, k_win, v_win, windows: Sequence[Window]
         _ptr(v_win), kw0.numel(), ctypes.byref(params) if nb else None, states, pl,
         _ptr(prefix_len_dev), _ptr(n_committed), _ptr(mask_state), _ptr(tokens),
         _ptr(block_phase), _ptr(out_tokens), int(mask_token_id), pers, app, _stream(stream)))
+    for i, w in enumerate(windows):
+        w.state = states[i]
+        prefix_len[i] = int(pl[i])
+    return [pers[i] for i in range(nb)], [app[i] for i in range(nb)]
+
+
+def d2f_decode_advance_paged(page_table, win_pages, new_pages, windows: Sequence[Window],
+                             prefix_len: list, n_committed, mask_state, tokens, block_phase,
+                             out_tokens, mask_token_id: int, n_heads_kv: int = 1,
+                             head_dim: int = 128, prefix_len_dev=None, stream=None):
+    """d2f_decode_advance for a paged cache: persisted blocks' pages join
+    page_table (no copy); new_pages (host ints, one per request) are taken by
+    appended blocks.  windows and prefix_len are updated in place.  Returns
+    (persisted, appended) per request."""
+    nb, table_stride = page_table.shape
+    mw = win_pages.shape[1]
+    if len(windows) != nb or len(prefix_len) != nb or len(new_pages) != nb:
+        raise ValueError("one window, prefix length and new page per request")
+    params = windows[0].params
+    dev = page_table.device
+    _contig("page_table", page_table, torch.int32, dev)
+    _contig("win_pages", win_pages, torch.int32, dev)
+    _contig("mask_state", mask_state, torch.uint8, dev)
+    _contig("tokens", tokens, torch.int32, dev)
+    _contig("block_phase", block_phase, torch.uint8, dev)
+    _contig("n_committed", n_committed, torch.int32, dev)
+    _contig("out_tokens", out_tokens, torch.int32, dev)
+    B = params.block_size
+    if (params.max_win_blocks != mw or mask_state.numel() != nb * mw * B or
+            out_tokens.numel() != nb * params.total_blocks * B):
+        raise ValueError("slot buffers do not match batch, window and total_blocks")
+    desc = make_desc(nb, n_heads_kv, n_heads_kv, head_dim, B, mw, table_stride * B,
+                     torch.bfloat16)
+    states = (WindowState * nb)()
+    for i, w in enumerate(windows):
+        states[i] = w.state
+    pl = _i32_array(prefix_len)
+    pers = (ctypes.c_int32 * nb)()
+    app = (ctypes.c_int32 * nb)()
+    _check(load().d2f_decode_advance_paged(
+        ctypes.byref(desc), _ptr(page_table), table_stride, _ptr(win_pages),
+        _i32_array(new_pages), ctypes.byref(params), states, pl, _ptr(prefix_len_dev),
+        _ptr(n_committed), _ptr(mask_state), _ptr(tokens), _ptr(block_phase), _ptr(out_tokens),
+        int(mask_token_id), pers, app, _stream(stream)))
     for i, w in enumerate(windows):
         w.state = states[i]
         prefix_len[i] = int(pl[i])

@@ -180,6 +180,8 @@ struct AdvReq {
   int32_t n_win_old;    // window blocks before
   int32_t n_win_new;    // window blocks after (persists and the append applied)
   int32_t copy_base;    // first KV-copy workgroup of this request
+  int32_t new_page;     // paged: page of an appended block
+  int32_t pad;
 };
 struct AdvArgs {
   void* kc;
@@ -195,6 +197,9 @@ struct AdvArgs {
   int32_t* prefix_dev;
   int32_t n_layers, hkv, head_dim, bsz, esize, wmax, max_win, total_blocks;
   int32_t n_req, req0, n_copy_wgs, mask_token_id;
+  int32_t* page_table;  // paged: [batch][table_stride]; nullptr for contiguous caches
+  int32_t* win_pages;   // paged: [batch][max_win]
+  int32_t table_stride;
   AdvReq req[kMaxReqPerLaunch];
 };
 hipError_t launch_decode_advance(const AdvArgs& a, hipStream_t s);

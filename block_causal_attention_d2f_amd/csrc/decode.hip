@@ -124,6 +124,19 @@ __device__ void advance_window(const AdvArgs& a, int i) {
   for (int k = threadIdx.x; k < a.max_win; k += blockDim.x)
     a.block_phase[rb * a.max_win + k] =
         k < r.n_win_new ? (uint8_t)((r.phase_bits >> k) & 1u) : (uint8_t)D2F_CONSERVATIVE;
+  if (a.page_table != nullptr && threadIdx.x == 0) {
+    // Paged: the persisted blocks' pages join the page table in order, the
+    // window's page list moves up, an appended block takes its new page, and
+    // slots past the window hold -1.  A handful of integers, one thread, in an
+    // order that reads every entry before it is overwritten.
+    int32_t* w = a.win_pages + rb * a.max_win;
+    int32_t* t = a.page_table + rb * a.table_stride + r.prefix / B;
+    for (int j = 0; j < r.persisted; ++j) t[j] = w[j];
+    const int kept_blocks = r.n_win_old - r.persisted;
+    for (int k = 0; k < kept_blocks; ++k) w[k] = w[k + r.persisted];
+    if (r.n_win_new > kept_blocks) w[r.n_win_new - 1] = r.new_page;
+    for (int k = max(r.n_win_new, kept_blocks); k < a.max_win; ++k) w[k] = -1;
+  }
   if (threadIdx.x == 0 && a.prefix_dev != nullptr) a.prefix_dev[rb] = r.prefix + shift;
 }
 
@@ -158,13 +171,19 @@ hipError_t launch_decode_advance(const AdvArgs& a, hipStream_t s) {
 
 using namespace d2f;
 
-extern "C" d2f_status_t d2f_decode_advance(
-    const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache, void* v_cache,
-    int64_t cache_layer_stride, const void* k_win, const void* v_win, int64_t win_layer_stride,
-    const d2f_window_params_t* params, d2f_window_t* windows_host, int32_t* prefix_len_host,
-    int32_t* prefix_len_dev, const int32_t* n_committed, uint8_t* mask_state, int32_t* tokens,
-    uint8_t* block_phase, int32_t* out_tokens, int32_t mask_token_id, int32_t* persisted_host,
-    int32_t* appended_host, d2f_stream_t stream) {
+namespace {
+
+// The step's bookkeeping for contiguous (paged == false) or paged caches.
+d2f_status_t advance_impl(const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache,
+                          void* v_cache, int64_t cache_layer_stride, const void* k_win,
+                          const void* v_win, int64_t win_layer_stride, int32_t* page_table,
+                          int32_t table_stride, int32_t* win_pages, const int32_t* new_pages_host,
+                          const d2f_window_params_t* params, d2f_window_t* windows_host,
+                          int32_t* prefix_len_host, int32_t* prefix_len_dev,
+                          const int32_t* n_committed, uint8_t* mask_state, int32_t* tokens,
+                          uint8_t* block_phase, int32_t* out_tokens, int32_t mask_token_id,
+                          int32_t* persisted_host, int32_t* appended_host, d2f_stream_t stream,
+                          bool paged) {
   d2f_status_t st = check_desc(desc);
   if (st != D2F_OK) return st;
   if (params == nullptr) return fail(D2F_ERR_INVALID_ARG, "window params are NULL");
@@ -178,29 +197,40 @@ extern "C" d2f_status_t d2f_decode_advance(
                 params->max_win_blocks, params->total_blocks);
   if (n_layers < 1) return fail(D2F_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
   if (desc->batch == 0) return D2F_OK;
-  if (k_cache == nullptr || v_cache == nullptr || k_win == nullptr || v_win == nullptr ||
-      windows_host == nullptr || prefix_len_host == nullptr || n_committed == nullptr ||
+  if (windows_host == nullptr || prefix_len_host == nullptr || n_committed == nullptr ||
       mask_state == nullptr || tokens == nullptr || block_phase == nullptr ||
       out_tokens == nullptr || persisted_host == nullptr || appended_host == nullptr)
     return fail(D2F_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (paged) {
+    if (page_table == nullptr || win_pages == nullptr || new_pages_host == nullptr ||
+        table_stride < 1)
+      return fail(D2F_ERR_INVALID_ARG, "page table, window pages or new pages are missing");
+  } else if (k_cache == nullptr || v_cache == nullptr || k_win == nullptr || v_win == nullptr) {
+    return fail(D2F_ERR_INVALID_ARG, "a required pointer is NULL");
+  }
   const int nb = desc->batch, B = desc->block_size, mw = desc->max_win_blocks;
   const long long wmax = (long long)mw * B;
-  const long long cache_layer = (long long)nb * desc->n_heads_kv * desc->cache_capacity *
-                                desc->head_dim;
-  const long long win_layer = (long long)nb * desc->n_heads_kv * wmax * desc->head_dim;
-  if (n_layers > 1 && (cache_layer_stride < cache_layer || win_layer_stride < win_layer))
-    return fail(D2F_ERR_INVALID_ARG, "layer strides smaller than one layer");
+  if (!paged) {
+    const long long cache_layer = (long long)nb * desc->n_heads_kv * desc->cache_capacity *
+                                  desc->head_dim;
+    const long long win_layer = (long long)nb * desc->n_heads_kv * wmax * desc->head_dim;
+    if (n_layers > 1 && (cache_layer_stride < cache_layer || win_layer_stride < win_layer))
+      return fail(D2F_ERR_INVALID_ARG, "layer strides smaller than one layer");
+    // A copy workgroup indexes its kCopySlices slices of at most Wmax rows with
+    // 32-bit counters of 2-byte elements.
+    if ((unsigned long long)wmax * desc->head_dim * (desc->dtype == D2F_BF16 ? 2 : 4) / 2 *
+            kCopySlices >= (1ULL << 32))
+      return fail(D2F_ERR_UNSUPPORTED, "window too large for the append copy");
+  }
   if ((long long)params->total_blocks * B > (1LL << 30))
     return fail(D2F_ERR_INVALID_ARG, "total_blocks * block_size too large");
-  // A copy workgroup indexes its kCopySlices slices of at most Wmax rows with
-  // 32-bit counters of 2-byte elements.
-  if ((unsigned long long)wmax * desc->head_dim * (desc->dtype == D2F_BF16 ? 2 : 4) / 2 *
-          kCopySlices >= (1ULL << 32))
-    return fail(D2F_ERR_UNSUPPORTED, "window too large for the append copy");
   for (int b = 0; b < nb; ++b) {
     const d2f_window_t& w = windows_host[b];
     if (prefix_len_host[b] < 0)
       return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d < 0", b, prefix_len_host[b]);
+    if (paged && prefix_len_host[b] % B != 0)
+      return fail(D2F_ERR_INVALID_ARG, "prefix_len[%d] = %d is not a whole number of blocks", b,
+                  prefix_len_host[b]);
     if (w.persisted < params->total_blocks &&
         (w.first < 0 || w.n_win < 1 || w.n_win > mw || w.first + w.n_win != w.started ||
          w.started > params->total_blocks))
@@ -221,9 +251,16 @@ extern "C" d2f_status_t d2f_decode_advance(
     if (win[b].persisted >= params->total_blocks) continue;  // finished request
     st = d2f_window_after_commit(params, &win[b], &nc[(size_t)b * mw], &pers[b], &app[b]);
     if (st != D2F_OK) return st;
-    if ((long long)prefix_len_host[b] + (long long)pers[b] * B > desc->cache_capacity)
+    if (paged) {
+      if (prefix_len_host[b] / B + pers[b] > table_stride)
+        return fail(D2F_ERR_CAPACITY, "request %d: page table full (%d + %d > %d)", b,
+                    prefix_len_host[b] / B, pers[b], table_stride);
+      if (app[b] && new_pages_host[b] < 0)
+        return fail(D2F_ERR_INVALID_ARG, "request %d appends a block but has no new page", b);
+    } else if ((long long)prefix_len_host[b] + (long long)pers[b] * B > desc->cache_capacity) {
       return fail(D2F_ERR_CAPACITY, "request %d: cache full (%d + %d > %lld)", b,
                   prefix_len_host[b], pers[b] * B, (long long)desc->cache_capacity);
+    }
   }
 
   const int esz = desc->dtype == D2F_BF16 ? 2 : 4;
@@ -252,6 +289,9 @@ extern "C" d2f_status_t d2f_decode_advance(
     a.n_req = std::min(kMaxReqPerLaunch, nb - b0);
     a.req0 = b0;
     a.mask_token_id = mask_token_id;
+    a.page_table = paged ? page_table : nullptr;
+    a.win_pages = paged ? win_pages : nullptr;
+    a.table_stride = table_stride;
     int copies = 0;
     for (int i = 0; i < a.n_req; ++i) {
       const int b = b0 + i;
@@ -266,7 +306,8 @@ extern "C" d2f_status_t d2f_decode_advance(
       for (int k = 0; k < r.n_win_new; ++k)
         if (win[b].phase[k] == D2F_AGGRESSIVE) r.phase_bits |= 1ull << k;
       r.copy_base = copies;
-      if (r.persisted > 0) copies += copy_workgroups(n_layers, desc->n_heads_kv);
+      r.new_page = paged ? new_pages_host[b] : -1;
+      if (!paged && r.persisted > 0) copies += copy_workgroups(n_layers, desc->n_heads_kv);
     }
     a.n_copy_wgs = copies;
     e = launch_decode_advance(a, (hipStream_t)stream);
@@ -280,4 +321,34 @@ extern "C" d2f_status_t d2f_decode_advance(
     appended_host[b] = app[b];
   }
   return D2F_OK;
+}
+
+}  // namespace
+
+extern "C" d2f_status_t d2f_decode_advance(
+    const d2f_attn_desc_t* desc, int32_t n_layers, void* k_cache, void* v_cache,
+    int64_t cache_layer_stride, const void* k_win, const void* v_win, int64_t win_layer_stride,
+    const d2f_window_params_t* params, d2f_window_t* windows_host, int32_t* prefix_len_host,
+    int32_t* prefix_len_dev, const int32_t* n_committed, uint8_t* mask_state, int32_t* tokens,
+    uint8_t* block_phase, int32_t* out_tokens, int32_t mask_token_id, int32_t* persisted_host,
+    int32_t* appended_host, d2f_stream_t stream) {
+  return advance_impl(desc, n_layers, k_cache, v_cache, cache_layer_stride, k_win, v_win,
+                      win_layer_stride, nullptr, 0, nullptr, nullptr, params, windows_host,
+                      prefix_len_host, prefix_len_dev, n_committed, mask_state, tokens,
+                      block_phase, out_tokens, mask_token_id, persisted_host, appended_host,
+                      stream, false);
+}
+
+extern "C" d2f_status_t d2f_decode_advance_paged(
+    const d2f_attn_desc_t* desc, int32_t* page_table, int32_t table_stride, int32_t* win_pages,
+    const int32_t* new_pages_host, const d2f_window_params_t* params, d2f_window_t* windows_host,
+    int32_t* prefix_len_host, int32_t* prefix_len_dev, const int32_t* n_committed,
+    uint8_t* mask_state, int32_t* tokens, uint8_t* block_phase, int32_t* out_tokens,
+    int32_t mask_token_id, int32_t* persisted_host, int32_t* appended_host,
+    d2f_stream_t stream) {
+  return advance_impl(desc, 1, nullptr, nullptr, 0, nullptr, nullptr, 0, page_table,
+                      table_stride, win_pages, new_pages_host, params, windows_host,
+                      prefix_len_host, prefix_len_dev, n_committed, mask_state, tokens,
+                      block_phase, out_tokens, mask_token_id, persisted_host, appended_host,
+                      stream, true);
 }

@@ -415,6 +415,26 @@ d2f_status_t d2f_decode_advance(const d2f_attn_desc_t* desc, int32_t n_layers, v
                                 int32_t* persisted_host, int32_t* appended_host,
                                 d2f_stream_t stream);
 
+/* d2f_decode_advance for a paged cache (see d2f_block_attn_paged): the
+ * persisted blocks' pages join page_table[b] in order (no K/V is copied), the
+ * window's page list win_pages[b] moves up, a block appended to request b's
+ * window takes page new_pages_host[b] (host int32 [batch]; read only for
+ * requests that append, which then must hold a page id >= 0), and slots past
+ * the window hold -1.  Everything else (schedule, slot rows, decoded tokens,
+ * prefix lengths, errors) is as d2f_decode_advance; prefix lengths must be
+ * whole blocks, and P/B + persisted <= table_stride (D2F_ERR_CAPACITY).  The
+ * caller knows which new pages were taken from appended_host. */
+d2f_status_t d2f_decode_advance_paged(const d2f_attn_desc_t* desc, int32_t* page_table,
+                                      int32_t table_stride, int32_t* win_pages,
+                                      const int32_t* new_pages_host,
+                                      const d2f_window_params_t* params,
+                                      d2f_window_t* windows_host, int32_t* prefix_len_host,
+                                      int32_t* prefix_len_dev, const int32_t* n_committed,
+                                      uint8_t* mask_state, int32_t* tokens, uint8_t* block_phase,
+                                      int32_t* out_tokens, int32_t mask_token_id,
+                                      int32_t* persisted_host, int32_t* appended_host,
+                                      d2f_stream_t stream);
+
 /* Static text for a status code. */
 const char* d2f_status_string(d2f_status_t status);
 

@@ -27,7 +27,7 @@ MASKED, COMMITTED = 0, 1
 
 
 def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_act, layers,
-         seed):
+         seed, paged=False):
     dev = "cuda"
     cap = max(prompt) + total * B
     wmax = mw * B
@@ -54,6 +54,27 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
     outt = torch.full((nb, total * B), -1, dtype=torch.int32, device=dev)
     logits = torch.full((nb * wmax, vocab), float("nan"), dtype=torch.float32)
     P, oP = list(prompt), list(prompt)
+    if paged:
+        # one page per block, randomly numbered; the prompt's pages first,
+        # then a free list from which every appended block takes one
+        assert all(p % B == 0 for p in prompt)
+        n_pages = sum(p // B for p in prompt) + nb * (total + 1) + 3
+        order = torch.randperm(n_pages, generator=torch.Generator().manual_seed(seed + 77)).tolist()
+        kp = torch.full((layers, n_pages, hkv, B, d), float("nan"), dtype=torch.bfloat16,
+                        device=dev)
+        vp = torch.full_like(kp, float("nan"))
+        ts = max(prompt) // B + total
+        pt = torch.full((nb, ts), -1, dtype=torch.int32)
+        wpg = torch.full((nb, mw), -1, dtype=torch.int32)
+        for b in range(nb):
+            for i in range(prompt[b] // B):
+                pg = order.pop()
+                pt[b, i] = pg
+                kp[:, pg] = kc[:, b, :, i * B:(i + 1) * B]
+                vp[:, pg] = vc[:, b, :, i * B:(i + 1) * B]
+            wpg[b, 0] = order.pop()
+        pt, wpg = pt.to(dev), wpg.to(dev)
+        free = order
     wins = [d2f.Window(B, mw, total, tau_add, tau_act) for _ in range(nb)]
     owins = [OW.Window(B, mw, total, tau_add, tau_act) for _ in range(nb)]
     omask = [np.zeros(B, np.uint8) for _ in range(nb)]
@@ -74,8 +95,18 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
                 kw[l, b, :, :len(pos)] = W.decode_window_kv(hkv, d, pos, step, 2, seed=s).to(dev)
                 vw[l, b, :, :len(pos)] = W.decode_window_kv(hkv, d, pos, step, 3, seed=s).to(dev)
             pl_attn = list(P)
-            d2f.d2f_block_attn(q[l], kc[l], vc[l], kw[l], vw[l], pl_attn, nwin, B, out=out,
-                               lse=lse)
+            if paged:
+                wh = wpg.cpu()
+                for b in live:   # the model writes the window's K/V into its pages
+                    for k in range(owins[b].n_win):
+                        pg = int(wh[b, k])
+                        kp[l, pg] = kw[l, b, :, k * B:(k + 1) * B]
+                        vp[l, pg] = vw[l, b, :, k * B:(k + 1) * B]
+                d2f.d2f_block_attn_paged(q[l], kp[l], vp[l], pt, wpg, pl_attn, nwin, out=out,
+                                         lse=lse)
+            else:
+                d2f.d2f_block_attn(q[l], kc[l], vc[l], kw[l], vw[l], pl_attn, nwin, B, out=out,
+                                   lse=lse)
             torch.cuda.synchronize()
             ro, rl = OA.block_attn(q[l].cpu(), okc[l], ovc[l], kw[l].cpu(), vw[l].cpu(), pl_attn,
                                    nwin, B, pairs=[(b, h) for b in live for h in range(hq)])
@@ -117,8 +148,14 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
         # -- the step's bookkeeping ----------------------------------------------------------
         okw = kw.float().cpu().numpy()
         ovw = vw.float().cpu().numpy()
-        pers, app = d2f.d2f_decode_advance(kc, vc, kw, vw, wins, P, ncd, ms, tk, ph, outt,
-                                           MASK_ID)
+        if paged:
+            new_pages = [free.pop() for _ in range(nb)]
+            pers, app = d2f.d2f_decode_advance_paged(pt, wpg, new_pages, wins, P, ncd, ms, tk, ph,
+                                                     outt, MASK_ID, n_heads_kv=hkv, head_dim=d)
+            free.extend(pg for pg, a in zip(new_pages, app) if not a)
+        else:
+            pers, app = d2f.d2f_decode_advance(kc, vc, kw, vw, wins, P, ncd, ms, tk, ph, outt,
+                                               MASK_ID)
         o = 0
         for b in range(nb):
             if owins[b].done:
@@ -160,10 +197,22 @@ def _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k_aggr, tau_add, tau_
         assert len(odec[b]) == total * B and MASK_ID not in odec[b]
         assert list(outh[b]) == odec[b]
         assert P[b] == prompt[b] + total * B
-    assert np.array_equal(kc.float().cpu().numpy(), okc)
-    assert np.array_equal(vc.float().cpu().numpy(), ovc)
+    if paged:   # the cache is the pages the table lists, in order
+        pth = pt.cpu()
+        for b in range(nb):
+            ids = [int(i) for i in pth[b, :P[b] // B]]
+            assert -1 not in ids and len(set(ids)) == len(ids)
+            gk = torch.cat([kp[:, i] for i in ids], dim=2).float().cpu().numpy()
+            gv = torch.cat([vp[:, i] for i in ids], dim=2).float().cpu().numpy()
+            assert np.array_equal(gk, okc[:, b, :, :P[b]])
+            assert np.array_equal(gv, ovc[:, b, :, :P[b]])
+        assert (wpg.cpu() == -1).all()
+    else:
+        assert np.array_equal(kc.float().cpu().numpy(), okc)
+        assert np.array_equal(vc.float().cpu().numpy(), ovc)
     tokens = nb * total * B
-    say(f"[decode-loop] nb={nb} L={layers} B={B} window={mw} blocks={total}: {step} steps, "
+    say(f"[decode-loop{' paged' if paged else ''}] nb={nb} L={layers} B={B} window={mw} "
+        f"blocks={total}: {step} steps, "
         f"{tokens / step:.2f} tokens per step, worst attention error {worst:.2e}")
     return step
 
@@ -187,3 +236,18 @@ def test_decode_loop_more_requests_than_one_launch():
     say("[decode-loop] start 70 requests")
     prompt = [(7 * b) % 23 for b in range(70)]
     _run(70, 2, 1, 64, 4, 2, 2, prompt, 300, 0.9, 1, 0.25, 0.75, 1, 5)
+
+
+@pytest.mark.parametrize("case", [
+    # nb, hq, hkv, d, B, window, total, prompt, vocab, tau, k_aggr, tau_add, tau_act, layers, seed
+    (2, 4, 2, 64, 16, 3, 5, [48, 16], 3000, 0.9, 2, 0.25, 0.75, 2, 6),
+    (3, 8, 8, 128, 8, 2, 4, [0, 24, 8], 2000, 0.9, 1, 0.1, 0.9, 1, 7),
+], ids=["paged-two-layers", "paged-B8"])
+def test_paged_decode_loop_matches_oracle(case):
+    """The same loop over a paged cache: window blocks live in pages, the
+    persist moves page ids, and the cache gathered through the page table
+    equals the oracle's byte for byte."""
+    nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k, ta, tc, layers, seed = case
+    say(f"[decode-loop paged] start {case}")
+    _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k, ta, tc, layers, seed, paged=True)
+
