@@ -95,6 +95,10 @@ def parse():
     ap.add_argument("--round-prefix", action="store_true",
                     help="round prefixes down to whole blocks (the paged layout's workload, "
                          "for a contiguous comparison)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="also time outside-block reuse: the window-only attention plus the "
+                         "log-space join, against the full call and the refresh of the outside "
+                         "part")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time complete multi-step decodes (pipelined active window) instead")
     ap.add_argument("--loop-blocks", type=int, default=8, help="blocks decoded per request")
@@ -452,6 +456,53 @@ def per_call_times(wl, reps, use_graph):
             wl.tokens[base:] = wl.tok0
         ms, _ = time_region(run)
         out[name] = ms / reps
+    return out
+
+
+def reuse_times(wl, reps, use_graph):
+    """Per-layer times of outside-block reuse: the full call, the outside part
+    (cache keys only, the refresh), the window-only part and the join."""
+    import torch
+    import block_causal_attention_d2f_amd as d2f
+    sh, n_sets = wl.sh, wl.n_sets
+    zero = [0] * sh.batch
+    lo = [0] * sh.batch
+    o_out, l_out = torch.empty_like(wl.out[0]), torch.empty_like(wl.lse[0])
+    o_win, l_win = torch.empty_like(wl.out[0]), torch.empty_like(wl.lse[0])
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+
+    def full():
+        for i in range(reps):
+            wl.attn(i % n_sets, 0)
+
+    def outside():
+        for i in range(reps):
+            s = wl.sets[i % n_sets]
+            d2f.d2f_block_attn_range(s["q"][0], s["k_cache"][0], s["v_cache"][0], lo,
+                                     sh.prefix_len, sh.n_win_blocks, sh.block_size, out=o_out,
+                                     lse=l_out, workspace=ws)
+
+    def window():
+        for i in range(reps):
+            s = wl.sets[i % n_sets]
+            d2f.d2f_block_attn(s["q"][0], s["k_cache"][0], s["v_cache"][0], s["k_win"][0],
+                               s["v_win"][0], zero, sh.n_win_blocks, sh.block_size, out=o_win,
+                               lse=l_win, workspace=ws)
+
+    def join():
+        for i in range(reps):
+            d2f.d2f_attn_combine(o_out, l_out, o_win, l_win, sh.n_win_blocks, sh.block_size,
+                                 out=wl.out[0], lse=wl.lse[0])
+
+    out = {}
+    for name, fn in (("full", full), ("outside_refresh", outside), ("window_only", window),
+                     ("join", join)):
+        run = capture(fn, use_graph)
+        run()
+        ms, _ = time_region(run)
+        out[name + "_us"] = round(ms / reps * 1e3, 3)
+    out["reuse_step_us"] = round(out["window_only_us"] + out["join_us"], 3)
+    out["speedup_when_reused"] = round(out["full_us"] / out["reuse_step_us"], 2)
     return out
 
 
@@ -848,6 +899,8 @@ def main():
                       "bytes": kv_b},
         "roofline": roof,
     }
+    if args.reuse and not args.paged:
+        rec["reuse"] = reuse_times(wl, args.call_reps, use_graph)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

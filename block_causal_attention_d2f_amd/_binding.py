@@ -29,6 +29,7 @@ EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_confidence_commit_workspace_size", "d2f_confidence_commit",
            "d2f_confidence_commit_ex", "d2f_prophet_threshold",
            "d2f_block_attn_paged", "d2f_kv_commit_paged", "d2f_decode_advance_paged",
+           "d2f_block_attn_range_workspace_size", "d2f_block_attn_range", "d2f_attn_combine",
            "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
            "d2f_status_string", "d2f_last_error", "d2f_version")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
@@ -95,6 +96,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "d2f_block_attn_paged": (_i32, [pdesc, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _pi32, _pi32,
                                         _vp, _vp, _vp, _sz, _vp]),
         "d2f_kv_commit_paged": (_i32, [pdesc, _vp, _i32, _vp, _i32, _pi32, _vp, _vp]),
+        "d2f_block_attn_range_workspace_size": (_i32, [pdesc, _pi32, _pi32, _pi32,
+                                                       ctypes.POINTER(_sz)]),
+        "d2f_block_attn_range": (_i32, [pdesc, _vp, _vp, _vp, _pi32, _pi32, _pi32, _vp, _vp,
+                                        _vp, _sz, _vp]),
+        "d2f_attn_combine": (_i32, [pdesc, _vp, _vp, _vp, _vp, _vp, _vp, _pi32, _vp]),
         "d2f_decode_advance_paged": (_i32, [pdesc, _vp, _i32, _vp, _pi32,
                                             ctypes.POINTER(WindowParams),
                                             ctypes.POINTER(WindowState), _pi32, _vp, _vp, _vp,
@@ -206,6 +212,56 @@ def _call_with_workspace(call, workspace, size, device):
     if st == 4:  # D2F_ERR_WORKSPACE
         st = call(torch.empty(max(size(), 256), dtype=torch.uint8, device=device))
     _check(st)
+
+
+def d2f_block_attn_range(q, k_cache, v_cache, key_lo, key_hi, n_win_blocks, block_size,
+                         out=None, lse=None, softmax_scale=0.0, workspace=None, stream=None):
+    """Window queries over cache keys [key_lo[b], key_hi[b]) only (see d2f.h).
+    Returns (out, lse)."""
+    nb, hq, wmax, d = q.shape
+    hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _contig(n, t, q.dtype, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    desc = make_desc(nb, hq, hkv, d, block_size, wmax // block_size, cap, q.dtype, softmax_scale)
+    lo, hi, nw = _i32_array(key_lo), _i32_array(key_hi), _i32_array(n_win_blocks)
+
+    def call(ws):
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        return load().d2f_block_attn_range(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
+                                           _ptr(v_cache), lo, hi, nw, _ptr(out), _ptr(lse),
+                                           _ptr(ws), nbytes, _stream(stream))
+
+    def size():
+        n = ctypes.c_size_t(0)
+        _check(load().d2f_block_attn_range_workspace_size(ctypes.byref(desc), lo, hi, nw,
+                                                          ctypes.byref(n)))
+        return int(n.value)
+    _call_with_workspace(call, workspace, size, q.device)
+    return out, lse
+
+
+def d2f_attn_combine(out_a, lse_a, out_b, lse_b, n_win_blocks, block_size, out=None, lse=None,
+                     stream=None):
+    """Log-space join of two attention results over disjoint keys (see d2f.h).
+    Returns (out, lse); out / lse may be out_a / lse_a."""
+    nb, hq, wmax, d = out_a.shape
+    for n, t in (("out_a", out_a), ("out_b", out_b)):
+        _contig(n, t, out_a.dtype, out_a.device)
+    for n, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        _contig(n, t, torch.float32, out_a.device)
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    desc = make_desc(nb, hq, hq, d, block_size, wmax // block_size, 1, out_a.dtype)
+    _check(load().d2f_attn_combine(ctypes.byref(desc), _ptr(out_a), _ptr(lse_a), _ptr(out_b),
+                                   _ptr(lse_b), _ptr(out), _ptr(lse), _i32_array(n_win_blocks),
+                                   _stream(stream)))
+    return out, lse
 
 
 def d2f_kv_commit(k_cache, v_cache, k_win, v_win, prefix_len: list, request: int,

@@ -154,8 +154,16 @@ long long host_key_tiles(long long P, long long k_end) {
 // every request's key splits.  Within a launch, requests are ordered by unit
 // size, largest first, so that the short units fill in behind the long ones.
 // Returns the workspace bytes needed.
+// key_off (key-range calls, else nullptr): the keys of request b are cache
+// rows [key_off[b], key_off[b] + prefix[b]) and no window keys; a request with
+// an empty range is idle.
 size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
-                      std::vector<Launch>& out) {
+                      std::vector<Launch>& out, const int32_t* key_off = nullptr) {
+  const bool cache_only = key_off != nullptr;
+  auto key_end = [&](int qt, long long qrows, long long P, long long W, long long G,
+                     long long B) {
+    return cache_only ? P : host_tile_key_end(qt, qrows, P, W, G, B);
+  };
   const int G = d->n_heads_q / d->n_heads_kv;
   const int B = d->block_size;
   // Query rows per unit: when no request has more than 32 query rows per KV
@@ -170,7 +178,7 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
     const int qtiles = (int)((G * W + qrows - 1) / qrows);
     for (int qt = 0; qt < qtiles; ++qt)
       total_tiles += (long long)d->n_heads_kv *
-                     host_key_tiles(prefix[b], host_tile_key_end(qt, qrows, prefix[b], W, G, B));
+                     host_key_tiles(prefix[b], key_end(qt, qrows, prefix[b], W, G, B));
   }
   const long long slots = std::max<long long>(
       1, (long long)(kSlotFill * (double)resident_workgroups(d->dtype, d->head_dim)));
@@ -185,14 +193,16 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
     std::vector<std::pair<long long, ReqInfo>> reqs;
     for (int b = b0; b < b1; ++b) {
       if (nwin[b] == 0) continue;  // idle request: no query rows
+      if (cache_only && prefix[b] == 0) continue;  // empty key range
       ReqInfo r{};
       r.b = b;
       r.prefix = prefix[b];
+      r.key_off = cache_only ? key_off[b] : 0;
       r.win = nwin[b] * B;
       r.qtiles = (G * r.win + qrows - 1) / qrows;
       // The last query tile sees the most keys; it sets the split count.
       const long long tiles = host_key_tiles(
-          r.prefix, host_tile_key_end(r.qtiles - 1, qrows, r.prefix, r.win, G, B));
+          r.prefix, key_end(r.qtiles - 1, qrows, r.prefix, r.win, G, B));
       r.nsplit = 1;
       if (tiles > kSplitFactor * chunk_tiles)
         r.nsplit = (int)std::min<long long>(tiles / kMinChunkTiles,
@@ -251,9 +261,10 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
                            const void* v_cache, const void* k_win, const void* v_win,
                            const int32_t* prefix_len_host, const int32_t* n_win_blocks_host,
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
-                           hipStream_t s, const PagedRefs* paged) {
+                           hipStream_t s, const PagedRefs* paged,
+                           const int32_t* key_off = nullptr) {
   std::vector<Launch> plan;
-  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
+  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan, key_off);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                 workspace == nullptr ? (size_t)0 : workspace_bytes, need);
@@ -286,6 +297,7 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
     a.n_groups = L.n_groups;
     a.remap = L.remap ? 1 : 0;
     a.c2 = scale * 1.4426950408889634f;
+    a.cache_only = key_off != nullptr ? 1 : 0;
     if (paged != nullptr) {
       a.page_table = paged->page_table;
       a.win_pages = paged->win_pages;
@@ -372,6 +384,112 @@ d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const vo
   return run_attention(desc, q, k_cache, v_cache, k_win, v_win, prefix_len_host,
                        n_win_blocks_host, out, lse, workspace, workspace_bytes,
                        (hipStream_t)stream, nullptr);
+}
+
+namespace {
+
+d2f_status_t check_ranges(const d2f_attn_desc_t* d, const int32_t* lo, const int32_t* hi,
+                          const int32_t* nwin, std::vector<int32_t>& len) {
+  if (d->batch == 0) return D2F_OK;
+  if (lo == nullptr || hi == nullptr || nwin == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "key ranges / n_win_blocks_host are NULL");
+  len.resize(d->batch);
+  for (int b = 0; b < d->batch; ++b) {
+    if (lo[b] < 0 || hi[b] < lo[b])
+      return fail(D2F_ERR_INVALID_ARG, "key range [%d, %d) of request %d is not a range", lo[b],
+                  hi[b], b);
+    if (hi[b] > d->cache_capacity)
+      return fail(D2F_ERR_CAPACITY, "key range of request %d ends at %d > capacity %lld", b,
+                  hi[b], (long long)d->cache_capacity);
+    if (nwin[b] < 0 || nwin[b] > d->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b, nwin[b],
+                  d->max_win_blocks);
+    len[b] = hi[b] - lo[b];
+  }
+  return D2F_OK;
+}
+
+}  // namespace
+
+d2f_status_t d2f_block_attn_range_workspace_size(const d2f_attn_desc_t* desc,
+                                                 const int32_t* key_lo_host,
+                                                 const int32_t* key_hi_host,
+                                                 const int32_t* n_win_blocks_host,
+                                                 size_t* bytes_out) {
+  if (bytes_out == nullptr) return fail(D2F_ERR_INVALID_ARG, "bytes_out is NULL");
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  std::vector<int32_t> len;
+  if ((st = check_ranges(desc, key_lo_host, key_hi_host, n_win_blocks_host, len)) != D2F_OK)
+    return st;
+  std::vector<Launch> plan;
+  *bytes_out = desc->batch == 0 ? 0
+                                : plan_attention(desc, len.data(), n_win_blocks_host, plan,
+                                                 key_lo_host);
+  return D2F_OK;
+}
+
+d2f_status_t d2f_block_attn_range(const d2f_attn_desc_t* desc, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* key_lo_host, const int32_t* key_hi_host,
+                                  const int32_t* n_win_blocks_host, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  std::vector<int32_t> len;
+  if ((st = check_ranges(desc, key_lo_host, key_hi_host, n_win_blocks_host, len)) != D2F_OK)
+    return st;
+  if (!head_dim_supported(desc->dtype, desc->head_dim))
+    return fail(D2F_ERR_UNSUPPORTED, "head_dim %d is not built for dtype %d", desc->head_dim,
+                (int)desc->dtype);
+  if (desc->batch == 0) return D2F_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr || lse == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "q, k_cache, v_cache, out and lse must not be NULL");
+  for (const void* p : {q, k_cache, v_cache, (const void*)out})
+    if (((uintptr_t)p % 16) != 0)
+      return fail(D2F_ERR_INVALID_ARG, "q/k/v/out buffers must be 16-byte aligned");
+  const size_t esz = desc->dtype == D2F_BF16 ? 2 : 4;
+  if (((size_t)desc->head_dim * esz) % 16 != 0)
+    return fail(D2F_ERR_UNSUPPORTED, "head_dim rows must be a multiple of 16 bytes");
+  return run_attention(desc, q, k_cache, v_cache, nullptr, nullptr, len.data(),
+                       n_win_blocks_host, out, lse, workspace, workspace_bytes,
+                       (hipStream_t)stream, nullptr, key_lo_host);
+}
+
+d2f_status_t d2f_attn_combine(const d2f_attn_desc_t* desc, const void* out_a, const float* lse_a,
+                              const void* out_b, const float* lse_b, void* out, float* lse,
+                              const int32_t* n_win_blocks_host, d2f_stream_t stream) {
+  d2f_status_t st = check_desc(desc);
+  if (st != D2F_OK) return st;
+  if (!head_dim_supported(desc->dtype, desc->head_dim))
+    return fail(D2F_ERR_UNSUPPORTED, "head_dim %d is not built for dtype %d", desc->head_dim,
+                (int)desc->dtype);
+  if (desc->batch == 0) return D2F_OK;
+  if (out_a == nullptr || lse_a == nullptr || out_b == nullptr || lse_b == nullptr ||
+      out == nullptr || lse == nullptr || n_win_blocks_host == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "a required pointer is NULL");
+  for (int b = 0; b < desc->batch; ++b)
+    if (n_win_blocks_host[b] < 0 || n_win_blocks_host[b] > desc->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b,
+                  n_win_blocks_host[b], desc->max_win_blocks);
+  const int wmax = desc->max_win_blocks * desc->block_size;
+  for (int b0 = 0; b0 < desc->batch; b0 += kMaxReqPerLaunch) {
+    CombineArgs a{};
+    a.out_a = out_a;
+    a.lse_a = lse_a;
+    a.out_b = out_b;
+    a.lse_b = lse_b;
+    a.out = out;
+    a.lse = lse;
+    a.hq = desc->n_heads_q;
+    a.wmax = wmax;
+    a.b0 = b0;
+    a.n_req = std::min(kMaxReqPerLaunch, desc->batch - b0);
+    for (int i = 0; i < a.n_req; ++i) a.win[i] = n_win_blocks_host[b0 + i] * desc->block_size;
+    hipError_t e = launch_combine(a, desc->head_dim, desc->dtype, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return D2F_OK;
 }
 
 d2f_status_t d2f_block_attn_paged(const d2f_attn_desc_t* desc, const void* q,

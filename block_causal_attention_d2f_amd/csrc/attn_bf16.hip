@@ -140,14 +140,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int rows = G * W;
   constexpr int QROWS = 32 * QB;  // query rows of the unit
   const int r0 = qt * QROWS;
-  const int k_end = tile_key_end(qt, QROWS, P, W, G, B);  // last key any row sees
-  const int k_full = P + min(W, ((r0 / G) / B + 1) * B);  // keys every row sees
+  const int k_end = unit_key_end(a, qt, QROWS, P, W, G, B);  // last key any row sees
+  const int k_full = a.cache_only ? P : P + min(W, ((r0 / G) / B + 1) * B);  // every row sees
   const int nct = cache_tiles(P);
   int t_lo, t_hi;
   split_tiles(nct + window_tiles(P, k_end), split, nsplit, t_lo, t_hi);
   const int n_tiles = t_hi - t_lo;
 
-  const size_t head_c = ((size_t)rb * a.hkv + kvh) * (size_t)a.cap * D;
+  const size_t head_c = (((size_t)rb * a.hkv + kvh) * (size_t)a.cap + a.req[ri].key_off) * D;
   const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
   const __bf16* kc = (const __bf16*)a.kc + head_c;
   const __bf16* vc = (const __bf16*)a.vc + head_c;
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     row_ok[qb] = row < rows;
     my_i[qb] = row_ok[qb] ? row / G : 0;
     my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
-    my_lim[qb] = P + min(W, (my_i[qb] / B + 1) * B);
+    my_lim[qb] = a.cache_only ? P : P + min(W, (my_i[qb] / B + 1) * B);
     if (row_ok[qb]) {
       const __bf16* qp =
           (const __bf16*)a.q + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;

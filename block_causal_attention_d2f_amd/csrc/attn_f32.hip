@@ -38,12 +38,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const int G = a.group, B = a.bsz;
   const int rows = G * W;
   const int r0 = qt * kQTile;
-  const int k_end = tile_key_end(qt, kQTile, P, W, G, B);
+  const int k_end = unit_key_end(a, qt, kQTile, P, W, G, B);
   const int nct = cache_tiles(P);
   int t_lo, t_hi;
   split_tiles(nct + window_tiles(P, k_end), split, nsplit, t_lo, t_hi);
 
-  const size_t head_c = ((size_t)rb * a.hkv + kvh) * (size_t)a.cap * D;
+  const size_t head_c = (((size_t)rb * a.hkv + kvh) * (size_t)a.cap + a.req[ri].key_off) * D;
   const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
   const float* kc = (const float*)a.kc + head_c;
   const float* vc = (const float*)a.vc + head_c;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
   const bool row_ok = my_row < rows;
   const int my_i = row_ok ? my_row / G : 0;
   const int my_h = kvh * G + (row_ok ? my_row % G : 0);
-  const int my_lim = P + min(W, (my_i / B + 1) * B);
+  const int my_lim = a.cache_only ? P : P + min(W, (my_i / B + 1) * B);
 
   for (int e = tid; e < kQTile * D; e += kAttnThreads) {
     const int rr = e / D, d = e % D;

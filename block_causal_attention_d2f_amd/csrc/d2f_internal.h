@@ -27,7 +27,7 @@ struct ReqInfo {
   int32_t nsplit;     // key-range splits per query tile (1 = final outputs)
   int32_t unit_base;  // first work unit of this request within the launch
   int32_t group_base; // first (kv_head, qtile) merge group within the launch
-  int32_t reserved;
+  int32_t key_off;    // key-range calls: first cache key of the range (else 0)
 };
 
 struct AttnArgs {
@@ -45,6 +45,7 @@ struct AttnArgs {
   int32_t n_req, n_units, n_groups;
   int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
   int32_t qrows;  // query rows per unit: kQTile, or 32 (bf16, narrow windows)
+  int32_t cache_only;  // key-range calls: the keys are cache rows [key_off, key_off + prefix)
   float c2;       // softmax scale * log2(e)
   // Paged K/V (bf16 only): kc/vc are page pools [n_pages][hkv][bsz][D];
   // cache key p of request b is row p % bsz of page page_table[b][p / bsz],
@@ -81,6 +82,11 @@ __device__ __forceinline__ int find_req_group(const AttnArgs& a, int g) {
 __device__ __forceinline__ int tile_key_end(int qt, int qrows, int P, int W, int G, int B) {
   const int r_last = min((qt + 1) * qrows, G * W) - 1;
   return P + min(W, ((r_last / G) / B + 1) * B);
+}
+// Key-range calls see no window keys: every row's keys end at P.
+__device__ __forceinline__ int unit_key_end(const AttnArgs& a, int qt, int qrows, int P, int W,
+                                            int G, int B) {
+  return a.cache_only ? P : tile_key_end(qt, qrows, P, W, G, B);
 }
 
 // Key tiles of a query tile.  The cache [0, P) and the visible part of the
@@ -122,6 +128,19 @@ hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
 int attn_bf16_wgs_per_cu(int head_dim);
 int attn_f32_wgs_per_cu(int head_dim);
 hipError_t launch_attn_merge(const AttnArgs& a, int head_dim, d2f_dtype_t dt, hipStream_t s);
+
+// Log-space composition of two attention results (combine.hip).
+struct CombineArgs {
+  const void* out_a;
+  const float* lse_a;
+  const void* out_b;
+  const float* lse_b;
+  void* out;
+  float* lse;
+  int32_t hq, wmax, b0, n_req;
+  int32_t win[kMaxReqPerLaunch];  // query rows of each request of the launch
+};
+hipError_t launch_combine(const CombineArgs& a, int head_dim, d2f_dtype_t dt, hipStream_t s);
 
 struct CommitArgs {
   const float* logits;

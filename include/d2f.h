@@ -157,6 +157,48 @@ d2f_status_t d2f_kv_commit(const d2f_attn_desc_t* desc, int32_t n_layers, void* 
                            int32_t block, int32_t* prefix_len_host, int32_t* prefix_len_dev,
                            d2f_stream_t stream);
 
+/* ---- Attention in segments: outside-block reuse ----
+ *
+ * [dLLM-survey] section "FlashBlock: 블록 외부 어텐션 캐싱": the attention of a
+ * block's queries over the keys outside the block can be cached across steps
+ * (its output and normaliser, a tensor that scales with the block, not the
+ * context) and joined each step with a freshly computed inside part by
+ * log-space composition; when too many tokens changed since it was cached it
+ * is recomputed instead.  In D2F the window's queries change every step, so
+ * reusing a cached outside part is an approximation; the composition itself
+ * is exact.
+ *
+ * d2f_block_attn_range: for request b, the window's query rows i < W_b attend
+ * to the cache keys [key_lo_host[b], key_hi_host[b]) only (all of them
+ * visible, no window keys).  Layouts, out, lse, scale and errors as
+ * d2f_block_attn; the cache arrays must hold key_hi_host[b] rows
+ * (D2F_ERR_CAPACITY otherwise); a request with an empty range or no window is
+ * idle (its rows untouched).  The window-only part is d2f_block_attn with
+ * prefix_len 0.  Workspace: d2f_block_attn_range_workspace_size.
+ */
+d2f_status_t d2f_block_attn_range_workspace_size(const d2f_attn_desc_t* desc,
+                                                 const int32_t* key_lo_host,
+                                                 const int32_t* key_hi_host,
+                                                 const int32_t* n_win_blocks_host,
+                                                 size_t* bytes_out);
+d2f_status_t d2f_block_attn_range(const d2f_attn_desc_t* desc, const void* q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* key_lo_host, const int32_t* key_hi_host,
+                                  const int32_t* n_win_blocks_host, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, d2f_stream_t stream);
+
+/* Join two attention results of the same query rows over disjoint key sets:
+ * per row i < W_b of request b, L = ln(e^L_a + e^L_b) and
+ * O = O_a e^(L_a - L) + O_b e^(L_b - L) (a side with L = -inf weighs 0).
+ * out_* and out are [batch][n_heads_q][Wmax][head_dim] in desc's dtype,
+ * lse_* and lse [batch][n_heads_q][Wmax] float; out / lse may alias out_a /
+ * lse_a or out_b / lse_b; rows i >= W_b are untouched.  Errors:
+ * D2F_ERR_INVALID_ARG, D2F_ERR_UNSUPPORTED (head_dim / dtype not built),
+ * D2F_ERR_HIP. */
+d2f_status_t d2f_attn_combine(const d2f_attn_desc_t* desc, const void* out_a, const float* lse_a,
+                              const void* out_b, const float* lse_b, void* out, float* lse,
+                              const int32_t* n_win_blocks_host, d2f_stream_t stream);
+
 /* ---- Paged KV cache: block completion as the persist signal ----
  *
  * [D2F-wiki] section "운영 관점" (KV cache management): completed blocks are

@@ -136,3 +136,45 @@ def block_attn_paged(q, k_pages, v_pages, page_table, win_pages, prefix_len, n_w
         kw[b, :, :n * B] = gather_pages(kp, wp[b] if n else [], n)
         vw[b, :, :n * B] = gather_pages(vp, wp[b] if n else [], n)
     return block_attn(q, kc, vc, kw, vw, prefix_len, n_win_blocks, B, scale=scale, pairs=pairs)
+
+
+def attn_range(q, k_cache, v_cache, key_lo, key_hi, n_win_blocks, block_size, scale=None):
+    """The window's query rows attend to cache keys [key_lo[b], key_hi[b])
+    only, all of them visible ([dLLM-survey] section "FlashBlock: 블록 외부
+    어텐션 캐싱": the part of the attention outside a block).  Returns (out,
+    lse) as block_attn does; rows past the window, and requests with an empty
+    range, are NaN."""
+    q = as_f64(q)
+    nb, hq, wmax, d = q.shape
+    kc, vc = as_f64(k_cache), as_f64(v_cache)
+    group = hq // kc.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full((nb, hq, wmax, d), np.nan)
+    lse = np.full((nb, hq, wmax), np.nan)
+    for b in range(nb):
+        lo, hi, W = int(key_lo[b]), int(key_hi[b]), int(n_win_blocks[b]) * int(block_size)
+        if hi <= lo or W == 0:
+            continue
+        for h in range(hq):
+            kk, vv = kc[b, h // group, lo:hi], vc[b, h // group, lo:hi]
+            o, l = attend(q[b, h, :W], kk, vv, np.ones((W, hi - lo), bool), scale)
+            out[b, h, :W] = o
+            lse[b, h, :W] = l
+    return out, lse
+
+
+def combine(out_a, lse_a, out_b, lse_b):
+    """Joint softmax attention of two disjoint key sets from the two parts:
+    L = log(e^L_a + e^L_b), O = O_a e^(L_a - L) + O_b e^(L_b - L) (the log-space
+    composition of [dLLM-survey] "FlashBlock"); a part with L = -inf has no keys
+    and weight 0."""
+    oa, ob = as_f64(out_a), as_f64(out_b)
+    la, lb = as_f64(lse_a), as_f64(lse_b)
+    with np.errstate(invalid="ignore"):
+        L = np.logaddexp(la, lb)
+        wa = np.where(np.isneginf(la), 0.0, np.exp(la - L))
+        wb = np.where(np.isneginf(lb), 0.0, np.exp(lb - L))
+    out = np.where(np.isneginf(la)[..., None], 0.0, oa) * wa[..., None] + \
+        np.where(np.isneginf(lb)[..., None], 0.0, ob) * wb[..., None]
+    return out, L
