@@ -320,6 +320,27 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
   return D2F_OK;
 }
 
+d2f_status_t check_ranges(const d2f_attn_desc_t* d, const int32_t* lo, const int32_t* hi,
+                          const int32_t* nwin, std::vector<int32_t>& len) {
+  if (d->batch == 0) return D2F_OK;
+  if (lo == nullptr || hi == nullptr || nwin == nullptr)
+    return fail(D2F_ERR_INVALID_ARG, "key ranges / n_win_blocks_host are NULL");
+  len.resize(d->batch);
+  for (int b = 0; b < d->batch; ++b) {
+    if (lo[b] < 0 || hi[b] < lo[b])
+      return fail(D2F_ERR_INVALID_ARG, "key range [%d, %d) of request %d is not a range", lo[b],
+                  hi[b], b);
+    if (hi[b] > d->cache_capacity)
+      return fail(D2F_ERR_CAPACITY, "key range of request %d ends at %d > capacity %lld", b,
+                  hi[b], (long long)d->cache_capacity);
+    if (nwin[b] < 0 || nwin[b] > d->max_win_blocks)
+      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b, nwin[b],
+                  d->max_win_blocks);
+    len[b] = hi[b] - lo[b];
+  }
+  return D2F_OK;
+}
+
 }  // namespace
 }  // namespace d2f
 
@@ -386,30 +407,6 @@ d2f_status_t d2f_block_attn(const d2f_attn_desc_t* desc, const void* q, const vo
                        (hipStream_t)stream, nullptr);
 }
 
-namespace {
-
-d2f_status_t check_ranges(const d2f_attn_desc_t* d, const int32_t* lo, const int32_t* hi,
-                          const int32_t* nwin, std::vector<int32_t>& len) {
-  if (d->batch == 0) return D2F_OK;
-  if (lo == nullptr || hi == nullptr || nwin == nullptr)
-    return fail(D2F_ERR_INVALID_ARG, "key ranges / n_win_blocks_host are NULL");
-  len.resize(d->batch);
-  for (int b = 0; b < d->batch; ++b) {
-    if (lo[b] < 0 || hi[b] < lo[b])
-      return fail(D2F_ERR_INVALID_ARG, "key range [%d, %d) of request %d is not a range", lo[b],
-                  hi[b], b);
-    if (hi[b] > d->cache_capacity)
-      return fail(D2F_ERR_CAPACITY, "key range of request %d ends at %d > capacity %lld", b,
-                  hi[b], (long long)d->cache_capacity);
-    if (nwin[b] < 0 || nwin[b] > d->max_win_blocks)
-      return fail(D2F_ERR_INVALID_ARG, "n_win_blocks[%d] = %d outside [0, %d]", b, nwin[b],
-                  d->max_win_blocks);
-    len[b] = hi[b] - lo[b];
-  }
-  return D2F_OK;
-}
-
-}  // namespace
 
 d2f_status_t d2f_block_attn_range_workspace_size(const d2f_attn_desc_t* desc,
                                                  const int32_t* key_lo_host,

@@ -14,7 +14,13 @@
  * then one pass over the vocabulary logits of the window positions that
  * decides which positions to commit (d2f_confidence_commit), and, when the
  * oldest window block is complete, moves that block's K/V into the cache
- * (d2f_kv_commit).
+ * (d2f_kv_commit).  Around these: the active-window schedule and the step's
+ * bookkeeping that turn them into pipelined multi-step decoding
+ * (d2f_window_*, d2f_decode_advance), other confidence measures and Prophet's
+ * early commit (d2f_confidence_commit_ex), a paged cache whose persist is a
+ * table update (d2f_block_attn_paged, d2f_kv_commit_paged,
+ * d2f_decode_advance_paged), and attention in segments with an exact join
+ * for outside-block reuse (d2f_block_attn_range, d2f_attn_combine).
  *
  * Conventions shared by every entry point:
  *  - Pointers named *_host are host memory read synchronously during the
