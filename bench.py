@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--loop-reps", type=int, default=3, help="timed complete decodes")
     ap.add_argument("--tau-add", type=float, default=0.25)
     ap.add_argument("--tau-act", type=float, default=0.75)
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="turn a rocprofv3 --pmc output dir with the MFMA counters of a bench "
+                         "run of --config into profiles/mfma_<config>.txt; needs no GPU")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE",
                                                               "RUN_FETCH", "RUN_WRITE"),
                     help="turn four rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of "
@@ -150,6 +153,74 @@ def _counter_means(d, counter):
             sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
             counts[k] = counts.get(k, 0) + 1
     return {k: sums[k] / counts[k] for k in sums}
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+N_CU, SIMD_PER_CU, N_XCD = 256, 4, 8
+
+
+def _dispatch_ns(d, counter, name_part):
+    """Average duration (ns) of the dispatches of kernels whose name holds
+    name_part, from the timestamps of a --pmc csv."""
+    import csv
+    import glob
+    tot, n = 0.0, 0
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                tot += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                n += 1
+    return tot / n if n else None
+
+
+def summarize_mfma(args):
+    """MFMA work and busy cycles of the attention kernel from counters."""
+    import workloads as W
+    d = args.summarize_mfma
+    vals = {c: _counter_means(d, c) for c in MFMA_COUNTERS}
+    cfg = W.config(args.config, block_size=args.block_size)
+    flops_alg = attn_flops(cfg["shape"])
+    kernels = {}
+    for name, mops in vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"].items():
+        if "attn_bf16_kernel" not in name:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        short = short.replace("void ", "").replace("d2f::", "")
+        ns = _dispatch_ns(d, MFMA_COUNTERS[0], short.split("<")[0])
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"].get(name, 0.0)
+        gui = vals["GRBM_GUI_ACTIVE"].get(name, 0.0)
+        flops = mops * 512.0
+        kernels[short] = {
+            "mfma_mops_bf16": round(mops), "mfma_flops": flops,
+            "algorithmic_flops": flops_alg,
+            "mfma_over_algorithmic": round(flops / flops_alg, 3),
+            "sq_valu_mfma_busy_cycles": round(busy), "sq_busy_cycles":
+                round(vals["SQ_BUSY_CYCLES"].get(name, 0.0)), "grbm_gui_active": round(gui),
+            "mfma_busy_frac": (round(busy / (gui / N_XCD * N_CU * SIMD_PER_CU), 4)
+                               if gui else None),
+            "clock_ghz_under_counters": round(gui / N_XCD / ns, 3) if gui and ns else None,
+            "avg_dispatch_us_under_counters": round(ns / 1e3, 3) if ns else None,
+            "mfma_tflops_under_counters": round(flops / ns / 1e3, 1) if ns else None}
+    key = traffic_key(args)
+    bs = "" if args.block_size is None else f" --block-size {args.block_size}"
+    hdr = (f"MFMA counters of the bf16 attention kernel, workload {key}.\n"
+           "Per-dispatch averages; mfma_flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;\n"
+           "GRBM_GUI_ACTIVE is summed over the 8 XCDs (per XCD it counts the kernel's clock\n"
+           "cycles: clock_ghz_under_counters), so mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES /\n"
+           "(GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs), the share of SIMD cycles with MFMA busy;\n"
+           "algorithmic_flops counts visible (query, key) pairs only (4 x head_dim each), so\n"
+           "mfma_over_algorithmic > 1 is padded rows and masked keys of partial tiles.\n"
+           "Command (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):\n"
+           f"  rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -- "
+           f"python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 "
+           "--no-cpu-baseline\n"
+           f"  python3 bench.py --config {args.config}{bs} --summarize-mfma <dir>\n")
+    path = os.path.join(ROOT, "profiles", f"mfma_{key}.txt")
+    with open(path, "w") as f:
+        f.write(hdr + "\n---\n" + json.dumps({"config": key, "source_hash": kernel_source_hash(),
+                                                "kernels": kernels}, indent=1) + "\n")
+    print(path)
 
 
 def summarize_counters(args):
@@ -787,6 +858,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
