@@ -9,7 +9,7 @@ layer's KV cache (d2f_kv_commit).  Inputs are resident in HBM before timing.
 Input sets rotate so that the timed steps read HBM rather than the 256 MB
 Infinity Cache, and every step gets its own pristine mask state.
 
-    python bench.py [--steps K] [--warmup W] [--config cfg2]
+    python bench.py [--steps K] [--warmup W] [--config llada_p512]
 
 prints one JSON line.  `value` is the step's compulsory HBM bytes (K/V once
 per KV head, Q, O, LSE, the masked rows' logits, the KV append) divided by
@@ -76,8 +76,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="cfg2", choices=["cfg2", "cfg3", "cfg4", "cfg5"])
-    ap.add_argument("--block-size", type=int, default=None, help="cfg4 block size (16/32/64)")
+    ap.add_argument("--config", default="llada_p512", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k"])
+    ap.add_argument("--block-size", type=int, default=None, help="dream_gqa block size (16/32/64)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
@@ -644,7 +644,7 @@ class DecodeLoop:
         import workloads as W
         import block_causal_attention_d2f_amd as d2f
         self.paged = args.paged
-        self.cfg = cfg = W.config("cfg3")
+        self.cfg = cfg = W.config("llada_batch16")
         sh = cfg["shape"]
         self.nb, self.hq, self.hkv, self.d, self.B = (sh.batch, sh.n_heads_q, sh.n_heads_kv,
                                                       sh.head_dim, sh.block_size)

@@ -22,9 +22,9 @@ def _check(shape, seed=0, pairs=None, label="", layer=0):
     return x, out, lse, stats
 
 
-def test_cfg1_tiny_fp32():
-    c = W.config("cfg1")
-    _check(c["shape"], label="cfg1")
+def test_tiny_f32():
+    c = W.config("tiny_f32")
+    _check(c["shape"], label="tiny_f32")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -83,34 +83,34 @@ def test_many_groups_with_one_long_request(d):
     _check(shape, pairs=pairs, label=f"many-groups-d{d}")
 
 
-def test_cfg2_llada_single_step():
-    c = W.config("cfg2")
-    _check(c["shape"], label="cfg2")
+def test_llada_p512_single_step():
+    c = W.config("llada_p512")
+    _check(c["shape"], label="llada_p512")
 
 
-def test_cfg3_ragged_batch_layers():
-    c = W.config("cfg3")
+def test_llada_batch16_layers():
+    c = W.config("llada_batch16")
     sh = c["shape"]
-    _check(sh, label="cfg3-L0", layer=0)
+    _check(sh, label="llada_batch16-L0", layer=0)
     rng = np.random.default_rng(3)
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, sh.batch, 24),
                                               rng.integers(0, sh.n_heads_q, 24))]
-    _check(sh, pairs=pairs, label="cfg3-L31-sampled", layer=31)
+    _check(sh, pairs=pairs, label="llada_batch16-L31-sampled", layer=31)
 
 
 @pytest.mark.parametrize("bsz", [16, 32, 64])
-def test_cfg4_dream_gqa(bsz):
-    c = W.config("cfg4", block_size=bsz)
+def test_dream_gqa(bsz):
+    c = W.config("dream_gqa", block_size=bsz)
     sh = c["shape"]
     pairs = [(0, h) for h in range(sh.n_heads_q)] + [(5, h) for h in (0, 6, 7, 13, 20, 27)]
-    _check(sh, pairs=pairs, label=f"cfg4-B{bsz}")
+    _check(sh, pairs=pairs, label=f"dream_gqa-B{bsz}")
 
 
-def test_cfg5_long_context():
-    c = W.config("cfg5")
+def test_llada_p32k():
+    c = W.config("llada_p32k")
     sh = c["shape"]
     pairs = [(0, h) for h in (0, 9, 17, 31)]
-    _check(sh, pairs=pairs, label="cfg5")
+    _check(sh, pairs=pairs, label="llada_p32k")
 
 
 def test_deterministic_and_later_blocks_do_not_leak():

@@ -23,28 +23,28 @@ def _cfg_case(name, bsz=None, tau=None, blocks=None):
         compare_commit(ci, got, t, c["k_aggr"], blocks=blocks, label=f"{name}-B{bsz}-tau{t}")
 
 
-def test_cfg1_tiny():
-    _cfg_case("cfg1")
+def test_tiny_f32():
+    _cfg_case("tiny_f32")
 
 
-def test_cfg2_llada_single_step():
-    _cfg_case("cfg2")
+def test_llada_p512_single_step():
+    _cfg_case("llada_p512")
 
 
-def test_cfg3_ragged_batch():
-    _cfg_case("cfg3")
+def test_llada_batch16():
+    _cfg_case("llada_batch16")
 
 
 @pytest.mark.parametrize("bsz", [16, 32, 64])
-def test_cfg4_dream_vocab(bsz):
+def test_dream_gqa_vocab(bsz):
     n_blocks = 24
     blocks = None if bsz == 16 else sorted({0, 1, 2, 9, 10, 11, 21, 22, 23})
     assert blocks is None or max(blocks) < n_blocks
-    _cfg_case("cfg4", bsz=bsz, blocks=blocks)
+    _cfg_case("dream_gqa", bsz=bsz, blocks=blocks)
 
 
-def test_cfg5_window_rows():
-    _cfg_case("cfg5")
+def test_llada_p32k_window_rows():
+    _cfg_case("llada_p32k")
 
 
 @pytest.mark.parametrize("vocab,ld_pad", [(1, 0), (7, 0), (513, 3), (8192, 0), (8193, 0),
@@ -154,7 +154,7 @@ def test_hand_worked_fixture_on_gpu():
 
 
 def test_deterministic():
-    ci = W.config_commit_inputs(W.config("cfg2"), device="cuda")
+    ci = W.config_commit_inputs(W.config("llada_p512"), device="cuda")
     a = run_commit(ci, 0.9, 1)
     b = run_commit(ci, 0.9, 1)
     for k in a:

@@ -10,7 +10,7 @@ pytestmark = pytest.mark.gpu
 
 def test_graph_replays_match_eager():
     import block_causal_attention_d2f_amd as d2f
-    c = W.config("cfg2")
+    c = W.config("llada_p512")
     sh = c["shape"]
     x = W.attn_inputs(sh, device="cuda", seed=4)
     ci = W.config_commit_inputs(c, device="cuda", seed=4)

@@ -71,13 +71,13 @@ def _shift_in_fresh_block(shape, x, it, seed=0):
         t[:, :, -B:] = W.fresh_block(shape, n, it, device="cuda", seed=seed)
 
 
-def test_cfg5_sequential_appends_reuse_exactness():
+def test_llada_p32k_sequential_appends_reuse_exactness():
     """64 blocks appended in sequence to the 32K-prefix cache.  After every
     append the window slides by one block; the surviving rows' outputs are
     compared with those computed before the append (exact reuse), and sampled
     heads are checked against the oracle on the grown cache."""
     import block_causal_attention_d2f_amd as d2f
-    c = W.config("cfg5")
+    c = W.config("llada_p32k")
     sh = c["shape"]
     B = sh.block_size
     x = W.attn_inputs(sh, device="cuda")
@@ -102,10 +102,10 @@ def test_cfg5_sequential_appends_reuse_exactness():
             h = (7 * it) % sh.n_heads_q
             pairs = [(0, h)]
             ro, rl = oracle_attn(sh, x, pairs=pairs)
-            compare_attn(sh, out, lse, ro, rl, pairs=pairs, label=f"cfg5-append{it}-h{h}")
+            compare_attn(sh, out, lse, ro, rl, pairs=pairs, label=f"llada_p32k-append{it}-h{h}")
         out_prev, lse_prev = out, lse
     assert prefix == [32768 + 64 * B] and pdev.cpu().tolist() == prefix
-    say(f"[cfg5 appends] 64 appends ok, worst surviving-row drift {worst:.3e}")
+    say(f"[llada_p32k appends] 64 appends ok, worst surviving-row drift {worst:.3e}")
 
 
 def test_reuse_oracle_vs_gpu_small():

@@ -17,8 +17,8 @@ TAUS = {"margin": 0.5, "neg_entropy": -2.0, "logit_gap": 5.0}
 
 
 @pytest.mark.parametrize("measure", ["margin", "neg_entropy", "logit_gap"])
-@pytest.mark.parametrize("cfg,bsz", [("cfg1", None), ("cfg2", None), ("cfg4", 16), ("cfg4", 64),
-                                     ("cfg5", None)])
+@pytest.mark.parametrize("cfg,bsz", [("tiny_f32", None), ("llada_p512", None), ("dream_gqa", 16), ("dream_gqa", 64),
+                                     ("llada_p32k", None)])
 def test_measures_on_the_workloads(measure, cfg, bsz):
     c = W.config(cfg, block_size=bsz)
     ci = W.config_commit_inputs(c, device="cuda", seed=7)
@@ -85,7 +85,7 @@ def test_prophet_one_group_and_ragged_last_group():
 def test_maxprob_through_the_extended_entry_matches_the_plain_one():
     """measure "maxprob" with an early threshold that never fires takes the
     second-largest accumulator path; its decisions equal the plain call's."""
-    c = W.config("cfg2")
+    c = W.config("llada_p512")
     ci = W.config_commit_inputs(c, device="cuda", seed=3)
     a = run_commit(ci, 0.9, 1)
     b = run_commit(ci, 0.9, 1, measure="maxprob", early_gap=[1e30])

@@ -217,30 +217,30 @@ def ragged_batch(batch: int, p_lo: int, p_hi: int, nw_lo: int, nw_hi: int, seed:
 def config(name: str, block_size: Optional[int] = None) -> dict:
     """Parameters of a named workload.  ``block_size`` picks one point of the
     Dream-shaped B sweep (16, 32 or 64)."""
-    if name == "cfg1":
+    if name == "tiny_f32":
         shape = make_shape(1, 2, 2, 32, 16, [48], [3], dtype="f32")
         return dict(name=name, workload="tiny fp32 D2F step", shape=shape, layers=1,
                     vocab=512, logit_std=2.0, boost=False, committed_frac=0.3,
                     phases=[AGGRESSIVE, AGGRESSIVE, CONSERVATIVE], taus=[0.9], k_aggr=1)
-    if name == "cfg2":
+    if name == "llada_p512":
         shape = make_shape(1, 32, 32, 128, 16, [512], [2], dtype="bf16")
         return dict(name=name, workload="LLaDA-8B-shaped single step", shape=shape, layers=1,
                     vocab=126464, logit_std=3.0, boost=True, committed_frac=0.0,
                     phases=window_phases([2]), taus=[0.9], k_aggr=1)
-    if name == "cfg3":
+    if name == "llada_batch16":
         prefix, nwin = ragged_batch(16, 256, 4096, 1, 4)
         shape = make_shape(16, 32, 32, 128, 16, prefix, nwin, dtype="bf16", max_win_blocks=4)
         return dict(name=name, workload="batched ragged decode at LLaDA-8B shape", shape=shape,
                     layers=32, vocab=126464, logit_std=3.0, boost=True, committed_frac=0.0,
                     phases=window_phases(nwin), taus=[0.9], k_aggr=1)
-    if name == "cfg4":
+    if name == "dream_gqa":
         b = 16 if block_size is None else int(block_size)
         assert b in (16, 32, 64)
         shape = make_shape(8, 28, 4, 128, b, [2048] * 8, [3] * 8, dtype="bf16")
         return dict(name=name, workload=f"Dream-7B-shaped GQA step, B={b}", shape=shape,
                     layers=1, vocab=152064, logit_std=3.0, boost=True, committed_frac=0.0,
                     phases=window_phases([3] * 8), taus=[0.8, 0.95], k_aggr=1)
-    if name == "cfg5":
+    if name == "llada_p32k":
         shape = make_shape(1, 32, 32, 128, 16, [32768], [4], dtype="bf16", extra_capacity=1024)
         return dict(name=name, workload="long-context step, 32K prefix", shape=shape, layers=1,
                     vocab=126464, logit_std=3.0, boost=True, committed_frac=0.0,
