@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llada_p512", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k"])
+    ap.add_argument("--config", default="llada_p512", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k", "llada_p128k"])
     ap.add_argument("--block-size", type=int, default=None, help="dream_gqa block size (16/32/64)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")

@@ -113,6 +113,13 @@ def test_llada_p32k():
     _check(sh, pairs=pairs, label="llada_p32k")
 
 
+def test_context_128k():
+    """A 131072-token prefix (the pages' open question about 100K+ contexts):
+    sampled heads against the oracle; every unread slot is NaN."""
+    shape = W.make_shape(1, 8, 8, 128, 16, [131072], [4], dtype="bf16")
+    _check(shape, pairs=[(0, 0), (0, 5)], label="context-128k")
+
+
 def test_deterministic_and_later_blocks_do_not_leak():
     shape = W.make_shape(2, 4, 2, 128, 16, [300, 1500], [4, 3], dtype="bf16")
     x = poisoned_inputs(shape, seed=11)

@@ -245,6 +245,12 @@ def config(name: str, block_size: Optional[int] = None) -> dict:
         return dict(name=name, workload="long-context step, 32K prefix", shape=shape, layers=1,
                     vocab=126464, logit_std=3.0, boost=True, committed_frac=0.0,
                     phases=window_phases([4]), taus=[0.9], k_aggr=1, n_kv_commits=64)
+    if name == "llada_p128k":
+        # The pages' open question about 100K+ token contexts, at the LLaDA shape.
+        shape = make_shape(1, 32, 32, 128, 16, [131072], [4], dtype="bf16", extra_capacity=1024)
+        return dict(name=name, workload="long-context step, 128K prefix", shape=shape, layers=1,
+                    vocab=126464, logit_std=3.0, boost=True, committed_frac=0.0,
+                    phases=window_phases([4]), taus=[0.9], k_aggr=1)
     raise KeyError(name)
 
 
