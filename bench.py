@@ -530,6 +530,39 @@ def per_call_times(wl, reps, use_graph):
     return out
 
 
+def per_call_spread(wl, reps):
+    """Per-launch duration spread of each call, in us: (p10, median, p90).
+
+    The host enqueues `reps` eager launches of the call, each between its own
+    pair of HIP events, behind a bounded spin kernel, so the queue is full
+    before the GPU reaches the first launch: the launches then run
+    back-to-back and each event pair brackets one call's GPU time (with the
+    event packets' own cost)."""
+    import numpy as np
+    import torch
+    n_sets = wl.n_sets
+    base = wl.masks.shape[0] - reps
+    calls = (("d2f_block_attn", lambda i: wl.attn(i % n_sets, 0)),
+             ("d2f_confidence_commit", lambda i: wl.commit(i % n_sets, base + i)),
+             ("d2f_kv_commit", lambda i: wl.kv(i % n_sets)))
+    out = {}
+    for name, call in calls:
+        wl.masks[base:] = wl.mask0
+        wl.tokens[base:] = wl.tok0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        for i in range(reps):
+            ev[i][0].record()
+            call(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        out[name] = tuple(round(float(x), 3) for x in np.percentile(us, [10, 50, 90]))
+    return out
+
+
 def reuse_times(wl, reps, use_graph):
     """Per-layer times of outside-block reuse: the full call, the outside part
     (cache keys only, the refresh), the window-only part and the join."""
@@ -896,6 +929,7 @@ def main():
     ms_step = ms_total / K
 
     calls = per_call_times(wl, args.call_reps, use_graph)
+    spread = per_call_spread(wl, args.call_reps)
     a_bytes = attn_bytes(sh)
     a_flops = attn_flops(sh)
     c_bytes = commit_bytes(wl.n_masked, wl.rows, wl.cfg["vocab"])
@@ -961,15 +995,21 @@ def main():
                    "launch": "hip-graph" if use_graph else "eager"},
         "step_bytes": step_bytes,
         "wall_ms_per_step": round(wall_ms / K, 5),
-        "attn": {"avg_us": round(t_attn * 1e6, 3), "tflops": round(attn_tflops, 3),
+        "attn": {"avg_us": round(t_attn * 1e6, 3),
+                 "p10_us": spread["d2f_block_attn"][0], "median_us": spread["d2f_block_attn"][1],
+                 "p90_us": spread["d2f_block_attn"][2], "tflops": round(attn_tflops, 3),
                  "frac_mfma": round(attn_tflops / PEAK_BF16_TFLOPS, 5),
                  "gbs": round(attn_gbs, 2), "frac_hbm": round(attn_gbs / PEAK_HBM_GBS, 4),
                  "kv_read_gbs": round(attn_kv_bytes(sh) / t_attn / 1e9, 2),
                  "flops": a_flops, "bytes": a_bytes, "intensity": round(ai, 2)},
-        "commit": {"avg_us": round(t_commit * 1e6, 3), "logit_gbs": round(commit_gbs, 2),
+        "commit": {"avg_us": round(t_commit * 1e6, 3),
+                   "p10_us": spread["d2f_confidence_commit"][0], "median_us": spread["d2f_confidence_commit"][1],
+                   "p90_us": spread["d2f_confidence_commit"][2], "logit_gbs": round(commit_gbs, 2),
                    "frac_hbm": round(commit_gbs / PEAK_HBM_GBS, 4), "bytes": c_bytes,
                    "masked_rows": wl.n_masked},
-        "kv_commit": {"avg_us": round(t_kv * 1e6, 3), "gbs": round(kv_b / t_kv / 1e9, 2),
+        "kv_commit": {"avg_us": round(t_kv * 1e6, 3),
+                      "p10_us": spread["d2f_kv_commit"][0], "median_us": spread["d2f_kv_commit"][1],
+                      "p90_us": spread["d2f_kv_commit"][2], "gbs": round(kv_b / t_kv / 1e9, 2),
                       "bytes": kv_b},
         "roofline": roof,
     }
