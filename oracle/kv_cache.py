@@ -15,8 +15,8 @@ import numpy as np
 def kv_commit(k_cache, v_cache, k_win, v_win, prefix_len, request, block_size):
     """Return (k_cache', v_cache', prefix_len') after appending window block 0
     of ``request`` (arrays [nb][Hkv][cap][D] and [nb][Hkv][Wmax][D])."""
-    k2 = np.array(k_cache, copy=True)
-    v2 = np.array(v_cache, copy=True)
+    k2 = np.asarray(k_cache).copy()
+    v2 = np.asarray(v_cache).copy()
     p = list(int(x) for x in prefix_len)
     b, B = int(request), int(block_size)
     P = p[b]
@@ -31,7 +31,7 @@ def kv_commit(k_cache, v_cache, k_win, v_win, prefix_len, request, block_size):
 def drop_oldest_block(x, request, block_size):
     """Window array with request's block 0 removed and the rest moved up one
     block (the state of the window after its oldest block left it)."""
-    y = np.array(x, copy=True)
+    y = np.asarray(x).copy()
     b, B = int(request), int(block_size)
     y[b, :, :-B] = np.asarray(x)[b, :, B:]
     y[b, :, -B:] = np.nan
@@ -44,8 +44,8 @@ def kv_commit_paged(page_table, win_pages, prefix_len, request, block_size):
     request's oldest window block becomes cache page P / B; the window's page
     list moves up by one and its last entry becomes -1; P grows by B.
     Returns (page_table', win_pages', prefix_len')."""
-    pt = np.array(page_table, copy=True)
-    wp = np.array(win_pages, copy=True)
+    pt = np.asarray(page_table).copy()
+    wp = np.asarray(win_pages).copy()
     p = [int(x) for x in prefix_len]
     b, B = int(request), int(block_size)
     P = p[b]

@@ -75,7 +75,7 @@ def test_paged_persist_is_the_contiguous_append():
     # with the same q rows) sees the same keys in the same order
     o0, l0 = OA.block_attn(x["q"], x["k_cache"], x["v_cache"], x["k_win"], x["v_win"],
                            sh.prefix_len, sh.n_win_blocks, 8)
-    q2 = np.array(x["q"], np.float64)
+    q2 = np.asarray(x["q"]).astype(np.float64)
     q2[1, :, 0:8] = q2[1, :, 8:16]
     o3, l3 = OA.block_attn_paged(q2, kp, vp, pt2, wp2, p2, nwin2, 8)
     assert np.array_equal(o0[1, :, 8:16], o3[1, :, 0:8])
