@@ -9,37 +9,9 @@ import torch
 import workloads as W
 from oracle import attention as OA
 from oracle import kv_cache as OK
-from parity import compare_attn, poisoned_inputs, say
+from parity import compare_attn, poisoned_inputs, say, to_pages
 
 pytestmark = pytest.mark.gpu
-
-
-def to_pages(sh, x, seed, spare=3):
-    """Scatter a contiguous cache and window into randomly numbered pages (on
-    the device); unused pages hold NaN."""
-    B, nb = sh.block_size, sh.batch
-    hkv, d = x["k_cache"].shape[1], x["k_cache"].shape[3]
-    need = sum(p // B for p in sh.prefix_len) + sum(sh.n_win_blocks)
-    n_pages = need + spare
-    g = torch.Generator().manual_seed(seed)
-    perm = torch.randperm(n_pages, generator=g).tolist()
-    kp = torch.full((n_pages, hkv, B, d), float("nan"), dtype=x["k_cache"].dtype, device="cuda")
-    vp = torch.full_like(kp, float("nan"))
-    ts = max(p // B for p in sh.prefix_len) + 2
-    pt = torch.full((nb, ts), -1, dtype=torch.int32)
-    wp = torch.full((nb, sh.max_win_blocks), -1, dtype=torch.int32)
-    for b in range(nb):
-        for i in range(sh.prefix_len[b] // B):
-            pg = perm.pop()
-            pt[b, i] = pg
-            kp[pg] = x["k_cache"][b, :, i * B:(i + 1) * B]
-            vp[pg] = x["v_cache"][b, :, i * B:(i + 1) * B]
-        for k in range(sh.n_win_blocks[b]):
-            pg = perm.pop()
-            wp[b, k] = pg
-            kp[pg] = x["k_win"][b, :, k * B:(k + 1) * B]
-            vp[pg] = x["v_win"][b, :, k * B:(k + 1) * B]
-    return kp, vp, pt.cuda(), wp.cuda()
 
 
 CASES = [
