@@ -156,7 +156,7 @@ def logits_normal(rows: int, vocab: int, std: float, boost: bool, device="cpu",
     if out is None:
         out = torch.empty((rows, vocab), device=device, dtype=torch.float32)
     out.normal_(0.0, std, generator=g)
-    if boost and rows > 0:
+    if boost and rows > 0 and vocab > 1:  # one column: no other entries to exceed
         gc = _gen("cpu", seed, layer, TID["boost_col"])
         gd = _gen("cpu", seed, layer, TID["boost_delta"])
         cols = torch.randint(0, vocab, (rows,), generator=gc)
