@@ -2,8 +2,10 @@
 d2f_block_attn (through the C ABI) against the fp64 oracle over batch, head
 counts, GQA group, head_dim, block size, ragged and empty prefixes (including
 the tile-boundary lengths 63/64/65/127/128), idle requests and spare cache
-capacity; and d2f_block_attn_paged against d2f_block_attn, bit for bit, on
-whole-block prefixes of the same draws."""
+capacity; d2f_block_attn_paged against d2f_block_attn, bit for bit, on
+whole-block prefixes of the same draws; and attention in segments (cache key
+ranges at random cut points joined to the window-only part) against the
+oracle's full attention."""
 import numpy as np
 import pytest
 import torch
@@ -71,3 +73,34 @@ def test_random_paged_equals_contiguous(k):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "outputs differ"
     assert torch.equal(l1, l2), "lse differs"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", range(4))
+def test_random_segments_compose_to_full_attention(dtype, k):
+    """The window-only part joined with 1..3 cache key ranges that tile
+    [0, P) at random cut points (empty ranges included, their parts start at
+    LSE = -inf) equals full block-causal attention, against the oracle."""
+    import block_causal_attention_d2f_amd as d2f
+    seed = 11000 + 100 * k + (0 if dtype == "f32" else 50)
+    sh = draw(seed, dtype)
+    rng = np.random.default_rng(seed + 1)
+    n_ranges = int(rng.integers(1, 4))
+    cuts = [[0] + sorted(int(c) for c in rng.integers(0, p + 1, n_ranges - 1)) + [p]
+            for p in sh.prefix_len]
+    say(f"--- random segments case seed={seed}: {sh}, cuts {cuts}")
+    x = poisoned_inputs(sh, seed=seed)
+    B, nwin = sh.block_size, sh.n_win_blocks
+    o, l = d2f.d2f_block_attn(x["q"], x["k_cache"], x["v_cache"], x["k_win"], x["v_win"],
+                              [0] * sh.batch, nwin, B)
+    for j in range(n_ranges):
+        lo = [c[j] for c in cuts]
+        hi = [c[j + 1] for c in cuts]
+        po = torch.zeros_like(x["q"])
+        pl = torch.full(x["q"].shape[:3], float("-inf"), device="cuda")
+        d2f.d2f_block_attn_range(x["q"], x["k_cache"], x["v_cache"], lo, hi, nwin, B, out=po,
+                                 lse=pl)
+        o, l = d2f.d2f_attn_combine(o, l, po, pl, nwin, B, out=o, lse=l)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_attn(sh, x)
+    compare_attn(sh, o, l, ref_o, ref_l, label=f"segments-{dtype}-{seed}")
