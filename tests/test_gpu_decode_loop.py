@@ -251,3 +251,31 @@ def test_paged_decode_loop_matches_oracle(case):
     say(f"[decode-loop paged] start {case}")
     _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, k, ta, tc, layers, seed, paged=True)
 
+
+
+def _draw_loop(seed, paged):
+    rng = np.random.default_rng(seed)
+    nb = int(rng.integers(1, 6))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    B = int(rng.choice([8, 16] if paged else [2, 4, 8, 16]))
+    mw = int(rng.integers(1, 5))
+    total = int(rng.integers(mw, mw + 4))
+    prompt = [int(rng.integers(0, 6)) * B if paged else int(rng.integers(0, 80)) for _ in range(nb)]
+    return (nb, hq, hkv, int(rng.choice([64, 128])), B, mw, total, prompt,
+            int(rng.integers(500, 4000)), float(rng.choice([0.8, 0.9, 0.95])),
+            int(rng.integers(1, 4)), float(rng.choice([0.0, 0.25, 0.5])),
+            float(rng.choice([0.3, 0.75, 0.95])), int(rng.integers(1, 3)), seed)
+
+
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("k", range(2))
+def test_random_decode_loops_match_oracle(paged, k):
+    """Seeded random loops: batch, heads, block size, window, sequence length,
+    prompts (whole blocks when paged), vocabulary, thresholds, k_aggr, layers."""
+    case = _draw_loop(13000 + 10 * k + (5 if paged else 0), paged)
+    say(f"[decode-loop random] start {case} paged={paged}")
+    nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, ka, ta, tc, layers, seed = case
+    steps = _run(nb, hq, hkv, d, B, mw, total, prompt, vocab, tau, ka, ta, tc, layers, seed,
+                 paged=paged)
+    assert steps >= total
