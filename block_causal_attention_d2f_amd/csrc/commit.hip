@@ -214,14 +214,15 @@ __device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& resul
 }
 
 // Combine the chunk partials of every row of one block into s_conf / s_idx
-// (and s_gap, the logit gap, when AUX is the second-largest value): one
-// thread per row loads kBatch partials at a time, all in flight, and folds
-// them in chunk order (a fixed order: the result does not depend on timing).
+// (and s_gap, the logit gap, when AUX is the second-largest value) and mark
+// the MASKED rows in s_live: one thread per row loads kBatch partials at a
+// time, all in flight, and folds them in chunk order (a fixed order: the
+// result does not depend on timing).
 // The loads do not wait for the mask state: a row that is not MASKED has no
 // partials written, and what is read for it is discarded.
 template <int AUX>
 __device__ void combine_rows(const CommitArgs& a, size_t row0, int B, float* s_conf, int* s_idx,
-                             float* s_gap) {
+                             float* s_gap, unsigned char* s_live) {
   constexpr int kBatch = 16;
   constexpr float kX0 = AUX == kAuxSecond ? kNegInf : 0.f;
   const int nck = a.n_chunks;
@@ -253,6 +254,7 @@ __device__ void combine_rows(const CommitArgs& a, size_t row0, int B, float* s_c
     }
     s_conf[p] = live ? c : 0.f;
     s_idx[p] = live ? ix : -1;
+    s_live[p] = live;
   }
 }
 
@@ -267,14 +269,18 @@ __global__ __launch_bounds__(kCommitThreads) void commit_decide_kernel(const Com
   const int B = a.block_size;
   const size_t row0 = (size_t)blk * B;
   const int tid = threadIdx.x;
+  // The phase goes through a vector load issued with the partials' loads
+  // (a uniform address would become a scalar load waited on at once).
+  int pidx = blk;
+  asm volatile("" : "+v"(pidx));
+  const unsigned char phase = a.block_phase[pidx];
   if (tid == 0) {
     s_cnt = 0;
     s_incomplete = 0;
   }
-  for (int p = tid; p < B; p += kCommitThreads) s_live[p] = a.mask_state[row0 + p] == D2F_MASKED;
-  combine_rows<AUX>(a, row0, B, s_conf, s_idx, s_gap);
+  combine_rows<AUX>(a, row0, B, s_conf, s_idx, s_gap, s_live);
   __syncthreads();
-  const bool aggressive = a.block_phase[blk] == D2F_AGGRESSIVE && a.k_aggr > 0;
+  const bool aggressive = phase == D2F_AGGRESSIVE && a.k_aggr > 0;
   const bool early = AUX == kAuxSecond && a.early_gap != nullptr;
   int cnt = 0, incomplete = 0;
   for (int p = tid; p < B; p += kCommitThreads) {
