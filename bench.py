@@ -530,6 +530,36 @@ def per_call_times(wl, reps, use_graph):
     return out
 
 
+# Width of the band around a threshold inside which the fp32 confidence and
+# the exact one may fall on different sides (the parity tests exclude these
+# decisions from the bit-exact comparison and count them).
+NEAR_BAND = {"maxprob": 1e-6, "margin": 1e-6, "neg_entropy": 5e-5, "logit_gap": 1e-5}
+
+
+def near_ties(wl):
+    """Commit decisions too close to call, from the GPU's own fp32 confidences
+    of the last commit call: MASKED rows within the measure's band of the
+    threshold (as the interface receives it, in float32), and aggressive
+    blocks whose k_aggr-th and (k_aggr+1)-th masked confidences are that close
+    while the latter does not clear the threshold."""
+    import numpy as np
+    import workloads as W
+    band = NEAR_BAND[wl.measure]
+    conf = wl.conf.cpu().double().numpy()
+    live = wl.mask0.cpu().numpy() == W.MASKED
+    tau = float(np.float32(wl.tau))
+    near_tau = int((live & (np.abs(conf - tau) <= band)).sum())
+    near_topk = 0
+    B, k = wl.sh.block_size, wl.k_aggr
+    if k > 0:
+        for j in np.flatnonzero(wl.phases.cpu().numpy() == W.AGGRESSIVE):
+            c = np.sort(conf[j * B:(j + 1) * B][live[j * B:(j + 1) * B]])[::-1]
+            if len(c) > k and c[k] <= tau and c[k - 1] - c[k] <= band:
+                near_topk += 1
+    return {"near_tau": near_tau, "near_topk": near_topk, "band": band,
+            "masked_rows": int(live.sum()), "source": "GPU fp32 confidences of the eager step"}
+
+
 def per_call_spread(wl, reps):
     """Per-launch duration spread of each call, in us: (p10, median, p90).
 
@@ -919,6 +949,7 @@ def main():
     # One eager step first (it also proves the path runs) on a spare mask set.
     wl.step(n_masks - 1)
     torch.cuda.synchronize()
+    ties = near_ties(wl)
 
     warm = capture(lambda: [wl.step(i) for i in range(Wu)], use_graph)
     timed = capture(lambda: [wl.step(Wu + i) for i in range(K)], use_graph)
@@ -1012,6 +1043,7 @@ def main():
                       "p90_us": spread["d2f_kv_commit"][2], "gbs": round(kv_b / t_kv / 1e9, 2),
                       "bytes": kv_b},
         "roofline": roof,
+        "near_ties": ties,
     }
     if args.reuse and not args.paged:
         rec["reuse"] = reuse_times(wl, args.call_reps, use_graph)

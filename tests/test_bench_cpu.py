@@ -1,0 +1,51 @@
+"""Host logic of bench.py that runs without a GPU: the near-tie count it
+reports next to the measurement."""
+import types
+
+import torch
+
+import bench
+
+
+def _wl(conf, phases, block_size, k_aggr, tau=0.9, measure="maxprob", masked=None):
+    n = len(conf)
+    mask0 = torch.zeros(n, dtype=torch.uint8)
+    if masked is not None:
+        mask0 = torch.tensor([0 if m else 1 for m in masked], dtype=torch.uint8)
+    return types.SimpleNamespace(measure=measure, tau=tau, k_aggr=k_aggr,
+                                 conf=torch.tensor(conf, dtype=torch.float32), mask0=mask0,
+                                 phases=torch.tensor(phases, dtype=torch.uint8),
+                                 sh=types.SimpleNamespace(block_size=block_size))
+
+
+def test_near_threshold_rows_are_counted():
+    # 0.9000004 and 0.8999996 lie within 1e-6 of float32(0.9); 0.9 + 1e-5 does not
+    wl = _wl([0.9000004, 0.8999996, 0.90001, 0.2], [0], 4, 0)
+    r = bench.near_ties(wl)
+    assert r["near_tau"] == 2 and r["near_topk"] == 0 and r["masked_rows"] == 4
+
+
+def test_committed_rows_are_not_counted():
+    wl = _wl([0.9000004, 0.9000004, 0.1, 0.2], [0], 4, 0, masked=[True, False, True, True])
+    assert bench.near_ties(wl)["near_tau"] == 1
+
+
+def test_near_topk_boundary_only_in_aggressive_blocks():
+    # block 0 aggressive: 1st and 2nd confidences 4e-7 apart, below tau -> near
+    # block 1 conservative: the same values do not count
+    # block 2 aggressive: the 2nd clears tau, so the boundary decides nothing
+    conf = [0.5000004, 0.5, 0.1, 0.05,
+            0.5000004, 0.5, 0.1, 0.05,
+            0.95, 0.9500004, 0.1, 0.05]
+    wl = _wl(conf, [1, 0, 1], 4, 1)
+    r = bench.near_ties(wl)
+    assert r["near_topk"] == 1 and r["near_tau"] == 0
+
+
+def test_k_aggr_two_and_measure_band():
+    # logit gap: band 1e-5; the 2nd and 3rd gaps are 5e-6 apart, below tau = 5
+    wl = _wl([3.0, 2.000005, 2.0, 0.5], [1], 4, 2, tau=5.0, measure="logit_gap")
+    r = bench.near_ties(wl)
+    assert r["near_topk"] == 1 and r["band"] == 1e-5
+    wl = _wl([3.0, 2.1, 2.0, 0.5], [1], 4, 2, tau=5.0, measure="logit_gap")
+    assert bench.near_ties(wl)["near_topk"] == 0
