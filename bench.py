@@ -13,7 +13,13 @@ Infinity Cache, and every step gets its own pristine mask state.
 
 prints one JSON line.  `value` is the step's compulsory HBM bytes (K/V once
 per KV head, Q, O, LSE, the masked rows' logits, the KV append) divided by
-the measured step time.
+the measured step time.  Per call it also reports the back-to-back average
+(`avg_us`, a HIP graph of repeated launches) and the spread of single
+launches (`p10_us`, `median_us`, `p90_us`); `roofline` for the call with the
+largest share of the step (with counter-measured HBM traffic when the
+summary under profiles/ was taken on these kernel sources); `near_ties`, the
+commit decisions too close to call; and `cpu_baseline`, the fp64 oracle on
+a bounded sample of the same workload on the host cores.
 """
 import argparse
 import json
