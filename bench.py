@@ -270,7 +270,8 @@ def summarize_counters(args):
            f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
            f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 --no-cpu-baseline\n"
            f"  python3 bench.py --config {args.config}{bs} --summarize-counters <4 dirs>\n"
-           "bench.py reports bytes_per_call as roofline.traffic only while source_hash matches.\n")
+           "bench.py reports bytes_per_call as roofline.traffic only while source_hash (the kernel\n"
+           "sources without comments or whitespace) matches.\n")
     with open(path, "w") as f:
         f.write(hdr + "\n---\n" + json.dumps(rec, indent=1) + "\n")
     print(path)
@@ -284,14 +285,19 @@ STEP_SOURCES = ("api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_merge.h", "att
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources of the per-step calls: counter-derived traffic
-    is only reported for the build it was measured on."""
+    """Hash of the HIP sources of the per-step calls, comments and whitespace
+    left out: counter-derived traffic is only reported for the code it was
+    measured on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     d = os.path.join(ROOT, "block_causal_attention_d2f_amd", "csrc")
     for f in STEP_SOURCES:
+        text = open(os.path.join(d, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

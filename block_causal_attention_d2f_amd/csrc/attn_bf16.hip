@@ -18,9 +18,10 @@
 //    filled and never waits for the in-flight tile before an LDS read.
 //  * The LDS rows are unpadded and their 16-byte chunks XOR-swizzled by row,
 //    which makes both LDS read patterns below free of bank conflicts.
-//  * Wave w works on query rows [32 (w & 1), +32) -- two 16-row MFMA blocks --
+//  * Wave w works on query rows [16 QB (w & 1), +16 QB) -- QB 16-row MFMA
+//    blocks: 2 for 64-row units, 1 for the 32-row units of narrow windows --
 //    and on key half (w >> 1) -- 32 keys -- of every tile, so each K or V
-//    fragment read from LDS feeds two MFMAs and each wave runs two
+//    fragment read from LDS feeds QB MFMAs and each wave runs 2 QB
 //    independent accumulation chains.  The two key halves are merged once,
 //    through LDS, at the end of the unit.
 //  * Scores are computed transposed, S^T = K Q^T: keys run along the MFMA M
@@ -36,6 +37,11 @@
 //  * A unit either covers all keys of its rows (writes O in bf16 and the LSE)
 //    or one key range (writes unnormalised O, running max and sum in fp32,
 //    merged exactly by attn_merge.hip).
+//  * Paged caches (PAGED != 0) change only the loader: the rows of each 1 KB
+//    direct load are found through the page tables, with the page ids of
+//    the next tile fetched while the current one is issued.  Key-range calls
+//    (cache_only) read cache keys [key_off, key_off + P) and no window keys,
+//    all of them visible.
 #include <type_traits>
 
 #include "d2f_internal.h"
