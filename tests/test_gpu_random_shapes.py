@@ -104,3 +104,36 @@ def test_random_segments_compose_to_full_attention(dtype, k):
     torch.cuda.synchronize()
     ref_o, ref_l = oracle_attn(sh, x)
     compare_attn(sh, o, l, ref_o, ref_l, label=f"segments-{dtype}-{seed}")
+
+
+def test_more_requests_than_one_launch():
+    """70 requests, past the 64 a launch carries: full attention, the paged
+    call and the segment join are each planned as two launches; all against
+    the oracle (paged: bit for bit against contiguous)."""
+    import block_causal_attention_d2f_amd as d2f
+    rng = np.random.default_rng(424242)
+    nb, B = 70, 8
+    prefix = [int(p) // B * B for p in rng.integers(0, 300, nb)]
+    nwin = [int(n) for n in rng.integers(0, 3, nb)]
+    nwin[0] = 2
+    sh = W.make_shape(nb, 4, 2, 64, B, prefix, nwin, dtype="bf16", max_win_blocks=2)
+    say(f"--- 70-request case: {sh}")
+    x = poisoned_inputs(sh, seed=4242)
+    out, lse = run_attn(sh, x, out_fill=7.0)
+    ref_o, ref_l = oracle_attn(sh, x)
+    compare_attn(sh, out, lse, ref_o, ref_l, label="70-requests")
+    kp, vp, pt, wp = to_pages(sh, x, seed=4242)
+    o2 = torch.full_like(x["q"], 7.0)
+    l2 = torch.full(x["q"].shape[:3], 7.0, device="cuda")
+    d2f.d2f_block_attn_paged(x["q"], kp, vp, pt, wp, prefix, nwin, out=o2, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+    wo, wl = d2f.d2f_block_attn(x["q"], x["k_cache"], x["v_cache"], x["k_win"], x["v_win"],
+                                [0] * nb, nwin, B)
+    co = torch.zeros_like(x["q"])
+    cl = torch.full(x["q"].shape[:3], float("-inf"), device="cuda")
+    d2f.d2f_block_attn_range(x["q"], x["k_cache"], x["v_cache"], [0] * nb, prefix, nwin, B,
+                             out=co, lse=cl)
+    jo, jl = d2f.d2f_attn_combine(wo, wl, co, cl, nwin, B)
+    torch.cuda.synchronize()
+    compare_attn(sh, jo, jl, ref_o, ref_l, label="70-requests-segments")
