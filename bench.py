@@ -217,7 +217,7 @@ def summarize_mfma(args):
            "(GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs), the share of SIMD cycles with MFMA busy;\n"
            "algorithmic_flops counts visible (query, key) pairs only (4 x head_dim each), so\n"
            "mfma_over_algorithmic > 1 is padded rows and masked keys of partial tiles.\n"
-           "Command (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`):\n"
+           "Command (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):\n"
            f"  rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -- "
            f"python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 "
            "--no-cpu-baseline\n"
@@ -263,7 +263,7 @@ def summarize_counters(args):
     hdr = (f"HBM traffic per call for workload {key} from rocprofv3 counters.\n"
            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are averaged per kernel and scaled by\n"
            "what the same counters read for a plain 512 MiB device copy (calibration).\n"
-           "Commands (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp`, each\n"
+           "Commands (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`, each\n"
            "counter in its own run):\n"
            "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"
            "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- python3 bench.py --copy-calibration\n"

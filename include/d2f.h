@@ -57,7 +57,7 @@ typedef enum {
   D2F_ERR_ORDER = 3,       /* kv_commit of a block other than the oldest one   */
   D2F_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required       */
   D2F_ERR_HIP = 5,         /* a HIP launch or runtime call failed              */
-  D2F_ERR_UNSUPPORTED = 6  /* valid, but not a shape this build handles        */
+  D2F_ERR_UNSUPPORTED = 6  /* valid, but not a shape this library handles      */
 } d2f_status_t;
 
 typedef enum { D2F_F32 = 0, D2F_BF16 = 1 } d2f_dtype_t;
