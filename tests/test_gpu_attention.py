@@ -38,6 +38,9 @@ def test_tiny_f32():
     (3, 4, 1, 128, 8, [1000, 64, 999], [4, 1, 2]),   # many key splits, GQA 4
     (1, 2, 2, 128, 64, [129], [3]),         # large B: window 192 rows > one query tile
     (1, 6, 2, 64, 48, [10], [2]),           # group 3, block straddles query tiles
+    (1, 4, 2, 64, 128, [300], [8]),         # 1024-row window: a block spans 4 query tiles
+    (1, 2, 2, 128, 256, [0], [4]),          # no cache, 1024-row window of 256-row blocks
+    (2, 3, 1, 64, 32, [65, 2000], [16, 7]), # 512-row window, group 3, ragged window lengths
 ])
 def test_edge_shapes(dtype, case):
     nb, hq, hkv, d, b, prefix, nwin = case

@@ -119,6 +119,18 @@ def test_large_vocab_and_largest_block():
     compare_commit(ci, got, 0.5, 5, label="B1024")
 
 
+@pytest.mark.parametrize("vocab", [1, 96])
+def test_many_blocks(vocab):
+    # 4096 blocks of 16 rows (65536 rows): a reduce grid of 65536 workgroups
+    # and a decide grid of 4096, with mixed phases and committed rows.
+    nb = 4096
+    phases = [W.AGGRESSIVE if k % 3 else W.CONSERVATIVE for k in range(nb)]
+    ci = W.commit_inputs(16 * nb, vocab, 16, phases, 2.0, True, committed_frac=0.3,
+                         device="cuda", seed=4096 + vocab)
+    got = run_commit(ci, 0.5, 2)
+    compare_commit(ci, got, 0.5, 2, label=f"blocks{nb}-V{vocab}")
+
+
 def test_hand_worked_fixture_on_gpu():
     rows, params, phases, blocks = [], {}, [], None
     for line in open(os.path.join(GOLDEN, "commit_worked_example.txt")):
