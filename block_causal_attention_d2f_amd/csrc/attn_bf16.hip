@@ -120,8 +120,15 @@ __device__ __forceinline__ void tile_barrier() {
 // PAGED: 0 contiguous K/V; otherwise rows are found through the page tables
 // (see AttnArgs): 1 for 8-row pages, 2 for pages of 16 rows or more, where the
 // 16 rows a wave loads of a tile always share one page.
-template <int D, int QB, int PAGED>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnArgs a) {
+// TG: tile groups of four waves.  1: one group takes every tile, two
+// workgroups per CU.  2: eight waves, group g takes
+// the unit's tiles g, g + 2, ... with its own two LDS stages, and the groups'
+// online-softmax states are joined exactly through LDS at the end.  For
+// launches with no more units than CUs, this puts two waves on every SIMD
+// without cutting the unit's keys into separately merged ranges.
+template <int D, int QB, int PAGED, int TG>
+__global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_kernel(
+    const AttnArgs a) {
   constexpr int RS = D * 2;                // LDS row bytes
   constexpr int KSTEPS = D / 32;           // MFMA k-steps over head_dim
   constexpr int DBLK = D / 16;             // 16-dim blocks of the output
@@ -132,6 +139,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   static_assert(LPW >= 1 && LPW * 4 * 1024 == TILE, "4 waves cover a tile in 1 KB blocks");
   static_assert(2 * DBLK * 64 * 4 * 2 * 4 <= 2 * TILE && 2 * 64 * 2 * 2 * 4 <= 2 * TILE,
                 "merge area fits the two stages");
+  static_assert(TG == 1 || TG == 2, "one or two tile groups");
+  constexpr int SB = TG * 2 * TILE;  // bytes per LDS stage: [group][K tile, V tile]
 
   const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
@@ -163,7 +172,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lc = lane & 15, lg = lane >> 4;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int qh = wave & 1, kh = (wave >> 1) & 1;
+  const int tg = TG == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave >> 2);  // tile group
 
   // Loader: tile rows are copied in 1 KB blocks, one direct load per wave
   // and block; lane l of block j carries the 16 bytes that belong at LDS
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     kb = (const char*)((in_cache ? kc : kw) + o);
     vb = (const char*)((in_cache ? vc : vw) + o);
   };
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave & 3);  // wave within its tile group
   // Paged rows: a 1 KB block holds RPB consecutive rows starting at a
   // multiple of RPB, and a page holds bsz rows with bsz a multiple of RPB,
   // so the rows of one direct load lie in one page and its base stays
@@ -209,7 +219,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     pg_row0 = (pi << pshift) - r0;
   };
   auto issue_paged = [&](auto J, int t) {
-    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, 2 * TILE>();
+    const unsigned sb =
+        (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>() + tg * 2 * TILE;
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
     int page = __builtin_amdgcn_readfirstlane(pg_page);
@@ -228,14 +239,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
       load_lds16((const char*)a.kc + pbase, off, sb + blk * 1024);
       load_lds16((const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
     }
-    fetch_pages(min(t + 1, t_hi - 1));
+    fetch_pages(min(t + TG, t_hi - 1));  // the group's next tile
   };
   auto issue = [&](auto J, int t) {
     if constexpr (PAGED != 0) {
       issue_paged(J, t);
       return;
     }
-    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, 2 * TILE>();
+    const unsigned sb =
+        (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>() + tg * 2 * TILE;
     const char *kb, *vb;
     int nv;
     tile_base(t, kb, vb, nv);
@@ -252,8 +264,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // The first tile is requested before the queries are loaded, so that its
   // latency and theirs overlap.  Tiles past the last re-read the last tile.
   auto tile_at = [&](int i) { return min(t_lo + i, t_hi - 1); };
-  if (PAGED != 0 && n_tiles > 0) fetch_pages(tile_at(0));
-  if (n_tiles > 0) issue(ic<0>{}, tile_at(0));
+  // Tiles of this wave's group: t_lo + tg, t_lo + tg + TG, ...; every group
+  // runs n_steps steps (the barriers are shared), idle when it has no tile.
+  [[maybe_unused]] const int n_g = (n_tiles - tg + TG - 1) / TG;
+  [[maybe_unused]] const int n_steps = (n_tiles + TG - 1) / TG;
+  [[maybe_unused]] auto gt = [&](int k) { return t_lo + TG * k + tg; };
+  if constexpr (TG == 1) {
+    if (PAGED != 0 && n_tiles > 0) fetch_pages(tile_at(0));
+    if (n_tiles > 0) issue(ic<0>{}, tile_at(0));
+  } else {
+    if (PAGED != 0 && n_g > 0) fetch_pages(gt(0));
+    if (n_g > 0) issue(ic<0>{}, gt(0));
+  }
 
   // This lane's two queries (MFMA column lc of the wave's two row blocks).
   int my_i[QB], my_h[QB], my_lim[QB];
@@ -293,7 +315,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   const float c2 = a.c2;
 
   auto compute = [&](auto J, int t) {
-    const char* Ks = stage_buf<decltype(J)::value, 2 * TILE>();
+    const char* Ks = stage_buf<decltype(J)::value, SB>() + tg * 2 * TILE;
     const lds_char* Vs = (const lds_char*)(Ks + TILE);
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
@@ -396,10 +418,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
     }
   };
 
-  // The tile after the last is issued too (re-reading the last tile, a cache
-  // hit) so that every wait covers exactly one tile; it is drained before the
-  // stages are reused below.
-  if (n_tiles > 0) {
+  if constexpr (TG == 2) {
+    // As below, per group: stage 0 of the group holds its tile k on entry to
+    // each pair of steps.  Nothing is requested past a group's last tile.
+    int k = 0;
+    for (; k + 2 <= n_steps; k += 2) {
+      tile_barrier();
+      if (k + 1 < n_g) issue(ic<1>{}, gt(k + 1));
+      if (wave_active && k < n_g) compute(ic<0>{}, gt(k));
+      tile_barrier();
+      if (k + 2 < n_g) issue(ic<0>{}, gt(k + 2));
+      if (wave_active && k + 1 < n_g) compute(ic<1>{}, gt(k + 1));
+    }
+    if (k < n_steps) {
+      tile_barrier();
+      if (wave_active && k < n_g) compute(ic<0>{}, gt(k));
+    }
+  } else if (n_tiles > 0) {
+    // The tile after the last is issued too (re-reading the last tile, a
+    // cache hit) so that every wait covers exactly one tile; it is drained
+    // before the stages are reused below.
     // Stage 0 holds tile i on entry to each pair (tile 0 was requested
     // before the query loads).  The barrier at the top of
     // a step both publishes the tile every wave loaded and retires the reads
@@ -430,30 +468,83 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(const AttnAr
   // wave of key half 0 with the same query half through LDS (same lane,
   // same register layout).
   tile_barrier();  // no load in flight, no tile read pending: the stages are free
-  float* xo = (float*)stage_buf<0, 2 * TILE>() + (size_t)qh * (QB * DBLK * 64 * 4);  // [qb][d][lane][4]
-  float* xml = (float*)stage_buf<1, 2 * TILE>() + qh * (QB * 64 * 2);
-  if (kh == 1 && wave_active) {
+  if constexpr (TG == 2) {
+    // Three waves per query half hand their state to the wave of key half 0
+    // in group 0: slot c = kh + 2 tg - 1.  Slots 0 and 1 of both query halves
+    // fill stage 0; slot 2 and the (m, l) pairs go to stage 1.
+    constexpr int SLOT = QB * DBLK * 64 * 4;  // floats of one wave's O
+    static_assert(4 * SLOT * 4 <= SB && (2 * SLOT + 6 * QB * 64 * 2) * 4 <= SB,
+                  "four-wave merge area fits the stages");
+    float* xo0 = (float*)stage_buf<0, SB>();
+    float* xo1 = (float*)stage_buf<1, SB>();
+    float* xml = xo1 + 2 * SLOT;
+    auto slot_o = [&](int c) { return c < 2 ? xo0 + (qh * 2 + c) * SLOT : xo1 + qh * SLOT; };
+    auto slot_ml = [&](int c) { return xml + (qh * 3 + c) * (QB * 64 * 2); };
+    const int c_me = kh + 2 * tg - 1;
+    if (c_me >= 0 && wave_active) {
+      float* xo = slot_o(c_me);
+      float* ml = slot_ml(c_me);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) = o[d][qb];
+        ml[(qb * 64 + lane) * 2 + 0] = m_run[qb];
+        ml[(qb * 64 + lane) * 2 + 1] = l_run[qb];
+      }
+    }
+    __syncthreads();
+    if (c_me >= 0 || !wave_active) return;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      float mc[3], lcs[3];
+      float m = m_run[qb];
 #pragma unroll
-      for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) = o[d][qb];
-      xml[(qb * 64 + lane) * 2 + 0] = m_run[qb];
-      xml[(qb * 64 + lane) * 2 + 1] = l_run[qb];
+      for (int c = 0; c < 3; ++c) {
+        mc[c] = slot_ml(c)[(qb * 64 + lane) * 2 + 0];
+        lcs[c] = slot_ml(c)[(qb * 64 + lane) * 2 + 1];
+        m = fmaxf(m, mc[c]);
+      }
+      const float w0 = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) o[d][qb] *= w0;
+      l_run[qb] *= w0;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const float wc = (mc[c] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mc[c] - m);
+        const float* xo = slot_o(c);
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+          o[d][qb] += *(const f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) * wc;
+        l_run[qb] += lcs[c] * wc;
+      }
+      m_run[qb] = m;
     }
-  }
-  __syncthreads();
-  if (kh == 1 || !wave_active) return;
+  } else {
+    float* xo = (float*)stage_buf<0, SB>() + (size_t)qh * (QB * DBLK * 64 * 4);  // [qb][d][lane][4]
+    float* xml = (float*)stage_buf<1, SB>() + qh * (QB * 64 * 2);
+    if (kh == 1 && wave_active) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float m1 = xml[(qb * 64 + lane) * 2 + 0], l1 = xml[(qb * 64 + lane) * 2 + 1];
-    const float m = fmaxf(m_run[qb], m1);
-    const float w0 = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
-    const float w1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-      o[d][qb] = o[d][qb] * w0 + *(const f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) * w1;
-    l_run[qb] = l_run[qb] * w0 + l1 * w1;
-    m_run[qb] = m;
+        for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) = o[d][qb];
+        xml[(qb * 64 + lane) * 2 + 0] = m_run[qb];
+        xml[(qb * 64 + lane) * 2 + 1] = l_run[qb];
+      }
+    }
+    __syncthreads();
+    if (kh == 1 || !wave_active) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m1 = xml[(qb * 64 + lane) * 2 + 0], l1 = xml[(qb * 64 + lane) * 2 + 1];
+      const float m = fmaxf(m_run[qb], m1);
+      const float w0 = (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m);
+      const float w1 = (m1 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+        o[d][qb] = o[d][qb] * w0 + *(const f32x4*)(xo + ((qb * DBLK + d) * 64 + lane) * 4) * w1;
+      l_run[qb] = l_run[qb] * w0 + l1 * w1;
+      m_run[qb] = m;
+    }
   }
 
 #pragma unroll
@@ -492,34 +583,39 @@ int attn_bf16_wgs_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2, 0>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2, 0, 1>,
                                                      kAttnThreads, 0);
   else if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2, 0>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2, 0, 1>,
                                                      kAttnThreads, 0);
   return e == hipSuccess ? n : 0;
 }
 
-template <int PAGED>
+template <int PAGED, int TG>
 hipError_t launch_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(a.n_units), block(kAttnThreads);
+  const dim3 grid(a.n_units), block(kAttnThreads * TG);
   const bool narrow = a.qrows == 32;
   if (head_dim == 128 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, PAGED>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, PAGED, TG>), grid, block, 0, s, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, PAGED>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, PAGED, TG>), grid, block, 0, s, a);
   else if (head_dim == 64 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, PAGED>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, PAGED, TG>), grid, block, 0, s, a);
   else if (head_dim == 64)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, PAGED>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, PAGED, TG>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
+template <int TG>
+hipError_t launch_tg(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {
+  if (!paged) return launch_bf16<0, TG>(a, head_dim, s);
+  return a.bsz >= 16 ? launch_bf16<2, TG>(a, head_dim, s) : launch_bf16<1, TG>(a, head_dim, s);
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {
-  if (!paged) return launch_bf16<0>(a, head_dim, s);
-  return a.bsz >= 16 ? launch_bf16<2>(a, head_dim, s) : launch_bf16<1>(a, head_dim, s);
+  return a.wide ? launch_tg<2>(a, head_dim, paged, s) : launch_tg<1>(a, head_dim, paged, s);
 }
 
 }  // namespace d2f

@@ -46,6 +46,7 @@ struct AttnArgs {
   int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
   int32_t qrows;  // query rows per unit: kQTile, or 32 (bf16, narrow windows)
   int32_t cache_only;  // key-range calls: the keys are cache rows [key_off, key_off + prefix)
+  int32_t wide;   // bf16: 1 = eight-wave workgroups, two tile groups
   float c2;       // softmax scale * log2(e)
   // Paged K/V (bf16 only): kc/vc are page pools [n_pages][hkv][bsz][D];
   // cache key p of request b is row p % bsz of page page_table[b][p / bsz],
