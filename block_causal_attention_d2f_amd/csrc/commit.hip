@@ -48,6 +48,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPerThread = kCommitChunk / kCommitThreads;  // 32 logits per thread
 constexpr int kWaves = kCommitThreads / 64;
 
+// Logit loads are marked non-temporal: every logit is read exactly once, so
+// the lines are not worth keeping in L2 or the Infinity Cache.  (Measured on
+// MI355X: the batched ragged workload's 291 MB pass 56.5 -> 50.9 us, Dream's
+// 934 MB pass 165 -> 145.6 us.)
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float load_stream(const float* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -100,7 +113,7 @@ __device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& resul
   if (VEC && n == kCommitChunk) {
 #pragma unroll
     for (int k = 0; k < kPerThread / 4; ++k) {
-      const float4 v = *(const float4*)(src + 4 * (tid + kCommitThreads * k));
+      const float4 v = load_stream4(src + 4 * (tid + kCommitThreads * k));
       x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
     }
   } else if (VEC) {
@@ -108,18 +121,18 @@ __device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& resul
     for (int k = 0; k < kPerThread / 4; ++k) {
       const int e0 = 4 * (tid + kCommitThreads * k);
       if (e0 + 3 < n) {
-        const float4 v = *(const float4*)(src + e0);
+        const float4 v = load_stream4(src + e0);
         x[4 * k + 0] = v.x; x[4 * k + 1] = v.y; x[4 * k + 2] = v.z; x[4 * k + 3] = v.w;
       } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[4 * k + c] = (e0 + c < n) ? src[e0 + c] : kNegInf;
+        for (int c = 0; c < 4; ++c) x[4 * k + c] = (e0 + c < n) ? load_stream(src + e0 + c) : kNegInf;
       }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int e = tid + kCommitThreads * k;
-      x[k] = (e < n) ? src[e] : kNegInf;
+      x[k] = (e < n) ? load_stream(src + e) : kNegInf;
     }
   }
   float m = kNegInf, m2 = kNegInf;
