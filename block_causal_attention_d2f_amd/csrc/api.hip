@@ -250,11 +250,10 @@ size_t plan_pass(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t*
 // kernel (two tile groups of four waves per unit), so that every SIMD holds
 // two waves of long, unsplit units.  Measured on MI355X: 8 requests with a
 // 2048-token prefix, 28 query and 4 KV heads (192 units of 33 tiles) took
-// 31 us against 35.6 us on four-wave workgroups.  A call that is split to
-// occupy the device keeps the four-wave kernel: a 512-token prefix with 32
-// heads, unsplit on the eight-wave kernel, averaged 11.1 us back to back
-// against 12.0 us for 3 key ranges and the merge, but a single launch took
-// about 1 us longer, and so did a step that depends on it.
+// 34.4-35.1 us against 39.7-39.9 us on four-wave workgroups.  A call that is
+// split to occupy the device keeps the four-wave kernel: a 512-token prefix
+// with 32 heads took 13.1 us unsplit on the eight-wave kernel against
+// 12.5 us for 3 key ranges and the merge (a dependent step 26.4 vs 25.3 us).
 size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
                       std::vector<Launch>& out, const int32_t* key_off = nullptr) {
   const long long resident = resident_workgroups(d->dtype, d->head_dim);
