@@ -34,6 +34,11 @@
 //    is raised lazily (only when a score exceeds it by 2^8), and each lane
 //    keeps its own partial sum, so the steady-state tile loop needs no
 //    cross-lane reduction at all.
+//  * Launches with no more units than CUs and no key split run eight waves
+//    per unit (TG = 2): two groups of four take alternate key tiles, each
+//    with its own stages, and their states are joined through LDS.
+//  * K/V tiles that no other query tile of the launch reads are loaded with
+//    the non-temporal cache policy.
 //  * A unit either covers all keys of its rows (writes O in bf16 and the LSE)
 //    or one key range (writes unnormalised O, running max and sum in fp32,
 //    merged exactly by attn_merge.hip).
@@ -140,11 +145,11 @@ __device__ __forceinline__ void tile_barrier() {
 // (see AttnArgs): 1 for 8-row pages, 2 for pages of 16 rows or more, where the
 // 16 rows a wave loads of a tile always share one page.
 // TG: tile groups of four waves.  1: one group takes every tile, two
-// workgroups per CU.  2: eight waves, group g takes
-// the unit's tiles g, g + 2, ... with its own two LDS stages, and the groups'
-// online-softmax states are joined exactly through LDS at the end.  For
-// launches with no more units than CUs, this puts two waves on every SIMD
-// without cutting the unit's keys into separately merged ranges.
+// workgroups per CU.  2: eight waves; group g takes the unit's tiles g, g + 2,
+// ... with its own two LDS stages, and the groups' online-softmax states are
+// joined exactly through LDS at the end.  For launches with no more units
+// than CUs, this puts two waves on every SIMD without cutting the unit's keys
+// into separately merged ranges.
 template <int D, int QB, int PAGED, int TG>
 __global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_kernel(
     const AttnArgs a) {
