@@ -40,6 +40,16 @@ ROTATE_BYTES = 640 << 20     # > 2x the 256 MB Infinity Cache
 SET_BUDGET_BYTES = 64 << 30  # device memory for the rotating input sets of the per-call timings
 
 
+def input_set_count(read_per_step, smallest_call, set_bytes):
+    """Rotating input sets: enough that the bytes streamed between two reads
+    of the same set exceed ROTATE_BYTES for the whole step; and, within
+    SET_BUDGET_BYTES of sets, also for the smallest single call (the per-call
+    timings repeat one call through every set)."""
+    n = 1 + math.ceil(ROTATE_BYTES / read_per_step)
+    per_call = 1 + math.ceil(ROTATE_BYTES / smallest_call)
+    return max(n, min(per_call, SET_BUDGET_BYTES // set_bytes))
+
+
 def attn_flops(sh):
     """Visible (query, key) pairs x 4 * head_dim (QK^T and PV)."""
     tot = 0.0
@@ -359,16 +369,10 @@ class Workload:
         self.set_bytes = (self.layers * es * sh.head_dim *
                           (sh.batch * sh.n_heads_q * sh.w_max + 2 * sh.batch * sh.n_heads_kv *
                            (sh.cache_capacity + sh.w_max)) + self.rows * self.cfg["vocab"] * 4)
-        # Enough input sets that the bytes streamed between two reads of the
-        # same set exceed the rotation budget (the cache cannot serve them).
-        # The per-call timings repeat one call through every set, so the
-        # smallest single call asks for more sets, within SET_BUDGET_BYTES
-        # (a workload whose sets are larger keeps the per-step count; its
-        # calls are then far larger than the cache anyway).
-        self.n_sets = 1 + math.ceil(ROTATE_BYTES / read_per_step)
+        # A workload whose sets exceed the budget keeps the per-step count;
+        # its calls are then far larger than the cache anyway.
         smallest = min(read_per_step, attn_bytes(sh), self.rows * self.cfg["vocab"] * 4)
-        per_call = 1 + math.ceil(ROTATE_BYTES / smallest)
-        self.n_sets = max(self.n_sets, min(per_call, SET_BUDGET_BYTES // self.set_bytes))
+        self.n_sets = input_set_count(read_per_step, smallest, self.set_bytes)
         self.sets = []
         for r in range(self.n_sets):
             xs = [W.attn_inputs(sh, layer=l, device=dev, seed=r * 7919) for l in range(self.layers)]

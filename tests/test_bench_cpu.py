@@ -1,5 +1,5 @@
 """Host logic of bench.py that runs without a GPU: the near-tie count it
-reports next to the measurement."""
+reports next to the measurement, and the number of rotating input sets."""
 import types
 
 import torch
@@ -49,3 +49,31 @@ def test_k_aggr_two_and_measure_band():
     assert r["near_topk"] == 1 and r["band"] == 1e-5
     wl = _wl([3.0, 2.1, 2.0, 0.5], [1], 4, 2, tau=5.0, measure="logit_gap")
     assert bench.near_ties(wl)["near_topk"] == 0
+
+
+MB = 1 << 20
+
+
+def _reuse_distance(n_sets, call_bytes):
+    # a call cycling through n sets reads n - 1 others between two reads of one set
+    return (n_sets - 1) * call_bytes
+
+
+def test_input_sets_outrun_the_cache_for_the_step_and_each_call():
+    # LLaDA single-step sizes: 25.6 MB read per step, 9.4 MB per attention call
+    n = bench.input_set_count(25.6 * MB, 9.4 * MB, 26 * MB)
+    assert _reuse_distance(n, 9.4 * MB) >= bench.ROTATE_BYTES
+    assert _reuse_distance(n, 25.6 * MB) >= bench.ROTATE_BYTES
+    assert n * 26 * MB <= bench.SET_BUDGET_BYTES
+
+
+def test_input_sets_stay_within_the_budget_for_large_sets():
+    # 35 GB sets (32 layers of a batched cache): the per-step rule alone applies
+    n = bench.input_set_count(19_000 * MB, 324 * MB, 35_000 * MB)
+    assert n == 2
+
+
+def test_input_sets_budget_caps_the_per_call_rule():
+    # per-call rule asks for 1 + ceil(640 / 1) = 641 sets; 1 GB sets cap it at 64
+    n = bench.input_set_count(2_000 * MB, 1 * MB, 1 << 30)
+    assert n == bench.SET_BUDGET_BYTES // (1 << 30)
