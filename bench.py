@@ -9,7 +9,12 @@ layer's KV cache (d2f_kv_commit).  Inputs are resident in HBM before timing.
 Input sets rotate so that the timed steps read HBM rather than the 256 MB
 Infinity Cache, and every step gets its own pristine mask state.
 
-    python bench.py [--steps K] [--warmup W] [--config llada_p512]
+    python bench.py [--steps K] [--warmup W] [--config llada_batch16]
+
+The default workload is the batched ragged decode at LLaDA-8B shape (16
+requests, prefixes ~ U(256, 4096), 1-4 window blocks of 16, 32 layers x 32
+heads x 128, vocabulary 126464); --config selects the single step, the
+Dream-shaped GQA sweep or the long prefixes.
 
 prints one JSON line.  `value` is the step's compulsory HBM bytes (K/V once
 per KV head, Q, O, LSE, the masked rows' logits, the KV append) divided by
@@ -93,7 +98,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llada_p512", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k", "llada_p128k"])
+    ap.add_argument("--config", default="llada_batch16", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k", "llada_p128k"])
     ap.add_argument("--block-size", type=int, default=None, help="dream_gqa block size (16/32/64)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")

@@ -8,7 +8,6 @@ the library is missing or a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Sequence
 
@@ -416,10 +415,6 @@ def prophet_threshold(progress: float) -> float:
 
 def version() -> int:
     return int(load().d2f_version())
-
-
-def softmax_scale_default(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)
 
 
 class Window:

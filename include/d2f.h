@@ -91,7 +91,11 @@ typedef struct {
 } d2f_attn_desc_t;
 
 /* Bytes of device workspace d2f_block_attn needs for these lengths (0 when
- * no key range is split).  Same argument rules as d2f_block_attn. */
+ * no key range is split), written to *bytes_out.  Same argument rules as
+ * d2f_block_attn.  The size comes back through an out-parameter, with a
+ * status as the return value, because 0 is a valid size (no split): a size
+ * returned directly could not tell "nothing needed" from "invalid
+ * arguments". */
 d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
                                            const int32_t* prefix_len_host,
                                            const int32_t* n_win_blocks_host,
@@ -255,7 +259,9 @@ d2f_status_t d2f_kv_commit_paged(const d2f_attn_desc_t* desc, int32_t* page_tabl
                                  d2f_stream_t stream);
 
 /* Bytes of device workspace d2f_confidence_commit and d2f_confidence_commit_ex
- * need (16-byte aligned; its contents need no initialisation). */
+ * need (16-byte aligned; its contents need no initialisation), written to
+ * *bytes_out; the status reports invalid sizes (as for
+ * d2f_block_attn_workspace_size). */
 d2f_status_t d2f_confidence_commit_workspace_size(int32_t n_rows, int32_t vocab,
                                                   size_t* bytes_out);
 

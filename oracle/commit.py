@@ -59,7 +59,6 @@ COMMITTED = 1
 CONSERVATIVE = 0
 AGGRESSIVE = 1
 
-NEAR_TIE = 1e-6
 MEASURES = ("maxprob", "margin", "neg_entropy", "logit_gap")
 # Width of the band around a threshold inside which fp32 and fp64 may decide
 # differently, per measure (see the design notes for the error bounds).

@@ -91,20 +91,3 @@ class Window:
                 self.phase[k] = AGGRESSIVE
         return persisted, appended
 
-
-def run_schedule(block_size, max_win_blocks, total_blocks, tau_add, tau_act, commits_of_step,
-                 max_steps=10000):
-    """Drive a Window with a function giving, for a step and the window state,
-    the positions committed per window block; returns the per-step trace
-    [(first, phases, committed_before, n_committed, persisted, appended)]."""
-    w = Window(block_size, max_win_blocks, total_blocks, tau_add, tau_act)
-    trace = []
-    step = 0
-    while not w.done:
-        assert step < max_steps, "schedule did not finish"
-        nc = commits_of_step(step, w)
-        before = (w.first, list(w.phase), list(w.committed))
-        p, a = w.after_commit(nc)
-        trace.append((before[0], before[1], before[2], list(nc), p, a))
-        step += 1
-    return trace

@@ -71,11 +71,29 @@ def _shift_in_fresh_block(shape, x, it, seed=0):
         t[:, :, -B:] = W.fresh_block(shape, n, it, device="cuda", seed=seed)
 
 
+# Scaled closeness of two bf16 attention outputs: mean |a - b| over mean |b|.
+# The kernel's own error is a few 1e-3 of the output's size: the
+# probabilities enter the PV product rounded to bf16 (relative error <= 2^-9
+# each) and the output is rounded to bf16 once more; an fp64 simulation of
+# exactly these roundings on this workload's shape gives 2.3e-3.  Dropping
+# or replacing the 16 keys of one appended block among 32K changes a
+# 32K-prefix output by about 2.0e-2 of its size (same simulation), so a bound
+# of 6e-3 tells the two apart, where the absolute bf16 tolerance (2e-2
+# against outputs of about 7e-3) cannot.  The measured values are printed.
+REL_MEAN = 6e-3
+
+
+def _rel_mean(a, b):
+    return float((a - b).abs().mean() / b.abs().mean())
+
+
 def test_llada_p32k_sequential_appends_reuse_exactness():
     """64 blocks appended in sequence to the 32K-prefix cache.  After every
-    append the window slides by one block; the surviving rows' outputs are
-    compared with those computed before the append (exact reuse), and sampled
-    heads are checked against the oracle on the grown cache."""
+    append: the cache's new rows equal the window block byte for byte; the
+    window slides by one block and the surviving rows' outputs are compared
+    with those computed before the append (exact reuse); one query head,
+    rotating through all 32, is checked against the oracle on the grown
+    cache."""
     import block_causal_attention_d2f_amd as d2f
     c = W.config("llada_p32k")
     sh = c["shape"]
@@ -84,10 +102,19 @@ def test_llada_p32k_sequential_appends_reuse_exactness():
     prefix = list(sh.prefix_len)
     pdev = torch.tensor(prefix, dtype=torch.int32, device="cuda")
     out_prev, lse_prev = run_attn(sh, x)
-    worst = 0.0
+    worst_drift = worst_rel = worst_oracle = 0.0
     for it in range(c["n_kv_commits"]):
+        p0 = prefix[0]
+        k_blk = x["k_win"][0, :, :B].clone()
+        v_blk = x["v_win"][0, :, :B].clone()
         d2f.d2f_kv_commit(x["k_cache"], x["v_cache"], x["k_win"], x["v_win"], prefix, 0, B,
                           prefix_len_dev=pdev)
+        torch.cuda.synchronize()
+        assert prefix[0] == p0 + B, it
+        assert torch.equal(x["k_cache"][0, :, p0:p0 + B].view(torch.uint8),
+                           k_blk.view(torch.uint8)), it
+        assert torch.equal(x["v_cache"][0, :, p0:p0 + B].view(torch.uint8),
+                           v_blk.view(torch.uint8)), it
         _shift_in_fresh_block(sh, x, it)
         sh.prefix_len = list(prefix)
         out, lse = run_attn(sh, x)
@@ -95,17 +122,27 @@ def test_llada_p32k_sequential_appends_reuse_exactness():
         a = out[:, :, :-B].float()
         b = out_prev[:, :, B:].float()
         diff = (a - b).abs()
-        worst = max(worst, float(diff.max()))
+        rel = _rel_mean(a, b)
+        worst_drift = max(worst_drift, float(diff.max()))
+        worst_rel = max(worst_rel, rel)
         assert float(diff.max()) <= 2e-2 and float(diff.mean()) <= 2e-3, (it, float(diff.max()))
+        assert rel <= REL_MEAN, (it, rel)
         assert float((lse[:, :, :-B] - lse_prev[:, :, B:]).abs().max()) <= 1e-3
-        if it in (0, 31, 63) or it % 8 == 3:
-            h = (7 * it) % sh.n_heads_q
-            pairs = [(0, h)]
-            ro, rl = oracle_attn(sh, x, pairs=pairs)
-            compare_attn(sh, out, lse, ro, rl, pairs=pairs, label=f"llada_p32k-append{it}-h{h}")
+        # The oracle on the grown cache, one head per append (all 32 twice).
+        h = it % sh.n_heads_q
+        pairs = [(0, h)]
+        ro, rl = oracle_attn(sh, x, pairs=pairs)
+        compare_attn(sh, out, lse, ro, rl, pairs=pairs, label=f"llada_p32k-append{it}-h{h}")
+        W_rows = sh.win_rows(0)
+        g = out[0, h, :W_rows].float().cpu().double()
+        r = torch.as_tensor(ro[0, h, :W_rows])
+        rel_o = float((g - r).abs().mean() / r.abs().mean())
+        worst_oracle = max(worst_oracle, rel_o)
+        assert rel_o <= REL_MEAN, (it, h, rel_o)
         out_prev, lse_prev = out, lse
     assert prefix == [32768 + 64 * B] and pdev.cpu().tolist() == prefix
-    say(f"[llada_p32k appends] 64 appends ok, worst surviving-row drift {worst:.3e}")
+    say(f"[llada_p32k appends] 64 appends ok, worst surviving-row drift {worst_drift:.3e} "
+        f"(mean/mean {worst_rel:.2e}), worst oracle mean/mean {worst_oracle:.2e}")
 
 
 def test_reuse_oracle_vs_gpu_small():
