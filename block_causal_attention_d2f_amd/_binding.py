@@ -30,7 +30,8 @@ EXPORTS = ("d2f_block_attn_workspace_size", "d2f_block_attn", "d2f_kv_commit",
            "d2f_block_attn_paged", "d2f_kv_commit_paged", "d2f_decode_advance_paged",
            "d2f_block_attn_range_workspace_size", "d2f_block_attn_range", "d2f_attn_combine",
            "d2f_window_init", "d2f_window_after_commit", "d2f_decode_advance",
-           "d2f_status_string", "d2f_last_error", "d2f_version")
+           "d2f_status_string", "d2f_last_error", "d2f_version",
+           "d2f_confidence_commit_noalloc")
 MAX_WINDOW = 64  # D2F_MAX_WINDOW
 MEASURES = {"maxprob": 0, "margin": 1, "neg_entropy": 2, "logit_gap": 3}  # d2f_conf_measure_t
 
@@ -111,6 +112,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                       ctypes.POINTER(WindowParams), ctypes.POINTER(WindowState),
                                       _pi32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _pi32, _pi32,
                                       _vp]),
+        "d2f_confidence_commit_noalloc": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _i32,
+                                                 _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
         "d2f_status_string": (ctypes.c_char_p, [_i32]),
         "d2f_last_error": (ctypes.c_char_p, []),
         "d2f_version": (_i32, []),
@@ -405,6 +408,38 @@ def d2f_confidence_commit(logits, mask_state, tokens, block_phase, block_size: i
             _ptr(block_phase), int(block_size), MEASURES[measure], ctypes.c_float(tau),
             int(k_aggr), int(mask_token_id), _ptr(early_gap), int(early_group_blocks),
             *args_tail))
+    return dict(n_committed=n_committed, block_complete=block_complete, conf=conf_out,
+                argmax=argmax_out)
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # D2F_NOALLOC_SCRATCH_BYTES
+
+
+def d2f_confidence_commit_noalloc(logits, mask_state, tokens, block_phase, block_size: int,
+                                  tau: float, k_aggr: int = 1, mask_token_id: int = 0,
+                                  conf_out=None, argmax_out=None, n_committed=None,
+                                  block_complete=None, stream=None):
+    """The commit pass of d2f_confidence_commit without a workspace: the
+    library's per-device scratch array holds the partials (see d2f.h).  With
+    every output buffer passed in, this call allocates nothing.
+    Returns dict(n_committed, block_complete, conf, argmax)."""
+    rows, vocab = logits.shape
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    dev = logits.device
+    _contig("mask_state", mask_state, torch.uint8, dev)
+    _contig("tokens", tokens, torch.int32, dev)
+    _contig("block_phase", block_phase, torch.uint8, dev)
+    n_blocks = rows // block_size if block_size > 0 else 0
+    if n_committed is None:
+        n_committed = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    if block_complete is None:
+        block_complete = torch.empty(n_blocks, dtype=torch.uint8, device=dev)
+    _check(load().d2f_confidence_commit_noalloc(
+        _ptr(logits), logits.stride(0), rows, vocab, _ptr(mask_state), _ptr(tokens),
+        _ptr(block_phase), int(block_size), ctypes.c_float(tau), int(k_aggr),
+        int(mask_token_id), _ptr(conf_out), _ptr(argmax_out), _ptr(n_committed),
+        _ptr(block_complete), _stream(stream)))
     return dict(n_committed=n_committed, block_complete=block_complete, conf=conf_out,
                 argmax=argmax_out)
 

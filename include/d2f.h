@@ -306,6 +306,30 @@ d2f_status_t d2f_confidence_commit(const float* logits, int64_t ld, int32_t n_ro
                                    uint8_t* block_complete, void* workspace,
                                    size_t workspace_bytes, d2f_stream_t stream);
 
+/* d2f_confidence_commit without a workspace argument, for callers that cannot
+ * allocate device memory: code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * semantics, outputs and errors as d2f_confidence_commit, computed by the
+ * same kernels.  The per-(row, vocabulary chunk) partials go to a scratch
+ * array of D2F_NOALLOC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends; nothing is allocated per call.
+ * Limit: d2f_confidence_commit_workspace_size(n_rows, vocab) must not exceed
+ * D2F_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. 16384 rows at a vocabulary of up to
+ * 262144), else D2F_ERR_WORKSPACE and nothing is launched.  Every call on a
+ * device shares that device's array: calls that overlap on one device (on
+ * two streams, or from two host threads without ordering) race and give
+ * undefined results.  The array is used on the device of `stream` (the
+ * current device for the NULL stream); its address is looked up on the first
+ * call on each device. */
+#define D2F_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+d2f_status_t d2f_confidence_commit_noalloc(const float* logits, int64_t ld, int32_t n_rows,
+                                           int32_t vocab, uint8_t* mask_state, int32_t* tokens,
+                                           const uint8_t* block_phase, int32_t block_size,
+                                           float tau, int32_t k_aggr, int32_t mask_token_id,
+                                           float* conf_out, int32_t* argmax_out,
+                                           int32_t* n_committed, uint8_t* block_complete,
+                                           d2f_stream_t stream);
+
 /* ---- Other confidence measures and Prophet's early commit ----
  *
  * [dLLM-survey] section "신뢰도를 넘어서: 궤적 일관성 디코딩(CCD)": decoders
