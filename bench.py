@@ -154,7 +154,8 @@ def copy_calibration(reps=5):
           flush=True)
 
 
-CALL_OF_KERNEL = (("attn_bf16_kernel", "d2f_block_attn"), ("attn_f32_kernel", "d2f_block_attn"),
+CALL_OF_KERNEL = (("attn_bf16_kernel", "d2f_block_attn"), ("attn_gqa_kernel", "d2f_block_attn"),
+                  ("attn_f32_kernel", "d2f_block_attn"),
                   ("attn_merge_kernel", "d2f_block_attn"),
                   ("vocab_reduce_kernel", "d2f_confidence_commit"),
                   ("commit_decide_kernel", "d2f_confidence_commit"),
@@ -205,7 +206,7 @@ def summarize_mfma(args):
     flops_alg = attn_flops(cfg["shape"])
     kernels = {}
     for name, mops in vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"].items():
-        if "attn_bf16_kernel" not in name:
+        if "attn_bf16_kernel" not in name and "attn_gqa_kernel" not in name:
             continue
         short = name.replace("(anonymous namespace)::", "").split("(")[0]
         short = short.replace("void ", "").replace("d2f::", "")
@@ -296,8 +297,8 @@ def summarize_counters(args):
 # Sources the three per-step calls are built from (planner, kernels, shared
 # declarations); the multi-step bookkeeping (window.hip, decode.hip) is not
 # among them.
-STEP_SOURCES = ("api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_merge.h", "attn_merge.hip",
-                "commit.hip", "kv_commit.hip", "d2f_internal.h")
+STEP_SOURCES = ("api.hip", "attn_bf16.hip", "attn_gqa.hip", "attn_lds.h", "attn_f32.hip",
+                "attn_merge.h", "attn_merge.hip", "commit.hip", "kv_commit.hip", "d2f_internal.h")
 
 
 def kernel_source_hash():

@@ -152,14 +152,16 @@ struct Launch {
   std::vector<ReqInfo> req;
   int n_units = 0, n_groups = 0;
   int qrows = kQTile;  // query rows per unit
+  int slot_rows = kQTile;  // partial-result rows per unit in the workspace
   bool any_split = false;
   bool remap = false;
   bool wide = false;   // eight-wave workgroups (two tile groups), bf16 only
+  bool gqa = false;    // grouped-query kernel (attn_gqa.hip), bf16 only
 };
 
 // Workspace of one launch: partial outputs, then partial (max, sum).
 size_t attn_partial_bytes(const Launch& L, int head_dim) {
-  return (size_t)L.n_units * kQTile * ((size_t)head_dim + 2) * sizeof(float);
+  return (size_t)L.n_units * L.slot_rows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 // Host copy of the kernels' key-tile count: cache and window tiled apart.
@@ -245,6 +247,84 @@ size_t plan_pass(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t*
   return ws;
 }
 
+// Calls that go to the grouped-query kernel: bf16 grouped-query calls on a
+// contiguous cache (the paged loader is the four-wave kernel's) with at
+// least kGqaMinRowsPerCU query rows per CU over the call, where a unit per
+// CU gives each K/V tile enough rows.  Measured on MI355X with 28 query / 4
+// KV heads, 8 requests and 2048 cached keys: 1344 rows per KV head (168 per
+// CU) 67-72 us against 81-85 us on the four-wave kernel; 672 rows (84 per
+// CU) 53 vs 51 us and 336 rows 42 vs 34 us, so those stay on it.
+constexpr long long kGqaMinRowsPerCU = 128;
+constexpr int kGqaMinGroup = 2;  // query heads per KV head
+bool use_gqa(const d2f_attn_desc_t* d, const int32_t* nwin, long long cus) {
+  if (d->dtype != D2F_BF16 || (d->head_dim != 64 && d->head_dim != 128) ||
+      d->n_heads_q / d->n_heads_kv < kGqaMinGroup)
+    return false;
+  long long rows = 0;
+  for (int b = 0; b < d->batch; ++b) rows += (long long)d->n_heads_q * nwin[b] * d->block_size;
+  return rows >= kGqaMinRowsPerCU * std::max<long long>(1, cus);
+}
+
+// Grouped-query plan (attn_gqa.hip): a unit is R query rows of one (request,
+// KV head) over all of its keys -- R a multiple of 16, at most kGqaMaxRows
+// -- one workgroup of eight waves, one workgroup per CU.  R is the launch's
+// query rows per CU, so that each CU gets about one unit and every K/V tile
+// it streams feeds as many rows as the launch allows.  Keys are never split
+// (the calls this kernel takes have at least kGqaMinRowsPerCU rows per CU,
+// so the units cover the CUs), and no workspace is needed.
+size_t plan_gqa(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
+                std::vector<Launch>& out, const int32_t* key_off, long long cus) {
+  const bool cache_only = key_off != nullptr;
+  const int G = d->n_heads_q / d->n_heads_kv;
+  const int B = d->block_size;
+  const int hkv = d->n_heads_kv;
+  cus = std::max<long long>(1, cus);
+  out.clear();
+  for (int b0 = 0; b0 < d->batch; b0 += kMaxReqPerLaunch) {
+    const int b1 = std::min(d->batch, b0 + kMaxReqPerLaunch);
+    auto active = [&](int b) { return nwin[b] > 0 && !(cache_only && prefix[b] == 0); };
+    long long rows = 0;
+    for (int b = b0; b < b1; ++b)
+      if (active(b)) rows += (long long)hkv * G * nwin[b] * B;
+    if (rows == 0) continue;
+    long long R = ((rows + cus - 1) / cus + 15) / 16 * 16;
+    R = std::min<long long>(kGqaMaxRows, std::max<long long>(16, R));
+    Launch L;
+    L.qrows = (int)R;
+    L.slot_rows = (int)R;
+    L.gqa = true;
+    std::vector<std::pair<long long, ReqInfo>> reqs;
+    for (int b = b0; b < b1; ++b) {
+      if (!active(b)) continue;
+      ReqInfo r{};
+      r.b = b;
+      r.prefix = prefix[b];
+      r.key_off = cache_only ? key_off[b] : 0;
+      r.win = nwin[b] * B;
+      r.qtiles = (int)((G * r.win + R - 1) / R);
+      r.nsplit = 1;
+      if (r.qtiles > 1) L.remap = true;
+      const long long tiles = host_key_tiles(
+          r.prefix, cache_only ? r.prefix
+                               : host_tile_key_end(r.qtiles - 1, R, r.prefix, r.win, G, B));
+      reqs.push_back({tiles, r});
+    }
+    std::stable_sort(reqs.begin(), reqs.end(),
+                     [](const auto& x, const auto& y) { return x.first > y.first; });
+    for (auto& pr : reqs) {
+      ReqInfo r = pr.second;
+      r.unit_base = L.n_units;
+      r.group_base = L.n_groups;
+      L.n_units += hkv * r.qtiles;
+      L.n_groups += hkv * r.qtiles;
+      L.req.push_back(r);
+    }
+    if (L.n_units == 0) continue;
+    out.push_back(std::move(L));
+  }
+  return 0;
+}
+
 // The launches of one call.  A bf16 call whose launches all have no more
 // units than the device has CUs and cut no key range runs the eight-wave
 // kernel (two tile groups of four waves per unit), so that every SIMD holds
@@ -255,7 +335,10 @@ size_t plan_pass(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t*
 // with 32 heads took 13.1 us unsplit on the eight-wave kernel against
 // 12.5 us for 3 key ranges and the merge (a dependent step 26.4 vs 25.3 us).
 size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
-                      std::vector<Launch>& out, const int32_t* key_off = nullptr) {
+                      std::vector<Launch>& out, const int32_t* key_off = nullptr,
+                      bool paged = false) {
+  if (!paged && use_gqa(d, nwin, device_cus()))
+    return plan_gqa(d, prefix, nwin, out, key_off, device_cus());
   const long long resident = resident_workgroups(d->dtype, d->head_dim);
   const size_t ws = plan_pass(d, prefix, nwin, out, key_off, kMinChunkTiles,
                               (long long)(kSlotFill * (double)resident));
@@ -303,7 +386,8 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
                            hipStream_t s, const PagedRefs* paged,
                            const int32_t* key_off = nullptr) {
   std::vector<Launch> plan;
-  const size_t need = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan, key_off);
+  const size_t need =
+      plan_attention(desc, prefix_len_host, n_win_blocks_host, plan, key_off, paged != nullptr);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(D2F_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                 workspace == nullptr ? (size_t)0 : workspace_bytes, need);
@@ -322,10 +406,11 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
     a.out = out;
     a.lse = lse;
     a.ws_o = (float*)workspace;
-    a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * kQTile * desc->head_dim
+    a.ws_ml = L.any_split ? (float*)workspace + (size_t)L.n_units * L.slot_rows * desc->head_dim
                           : nullptr;
     a.cap = desc->cache_capacity;
     a.qrows = L.qrows;
+    a.slot_rows = L.slot_rows;
     a.hq = desc->n_heads_q;
     a.hkv = desc->n_heads_kv;
     a.group = desc->n_heads_q / desc->n_heads_kv;
@@ -348,7 +433,8 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
       a.page_shift = sh;
     }
     for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
-    hipError_t e = desc->dtype == D2F_BF16
+    hipError_t e = L.gqa ? launch_attn_gqa(a, desc->head_dim, s)
+                   : desc->dtype == D2F_BF16
                        ? launch_attn_bf16(a, desc->head_dim, paged != nullptr, s)
                        : launch_attn_f32(a, desc->head_dim, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -413,7 +499,11 @@ d2f_status_t d2f_block_attn_workspace_size(const d2f_attn_desc_t* desc,
   if (st != D2F_OK) return st;
   if ((st = check_lengths(desc, prefix_len_host, n_win_blocks_host)) != D2F_OK) return st;
   std::vector<Launch> plan;
-  *bytes_out = plan_attention(desc, prefix_len_host, n_win_blocks_host, plan);
+  // The size covers both the contiguous and the paged call on these lengths
+  // (their plans may differ).
+  *bytes_out = std::max(plan_attention(desc, prefix_len_host, n_win_blocks_host, plan),
+                        plan_attention(desc, prefix_len_host, n_win_blocks_host, plan, nullptr,
+                                       true));
   return D2F_OK;
 }
 

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_f32_kernel(const AttnArgs a
     return;
   }
   if (row_ok) {
-    const size_t row_slot = (size_t)u * kQTile + r;
+    const size_t row_slot = (size_t)u * a.slot_rows + r;
     float* wp = a.ws_o + row_slot * D;
 #pragma unroll
     for (int k = 0; k < D / 4; ++k) wp[sub + 4 * k] = acc[k];

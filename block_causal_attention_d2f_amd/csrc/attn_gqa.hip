@@ -1,0 +1,391 @@
+// Block-causal window attention for grouped-query launches: bf16 inputs,
+// fp32 accumulation, v_mfma_f32_16x16x32_bf16, many query rows per K/V tile.
+//
+// What is computed is what attn_bf16.hip computes ([D2F-wiki] "블록 단위 인과
+// 어텐션"; [D2F-review] "쉽게 이해하기"): window row i of a request sees every
+// cached key and the window keys of its own block and of every earlier
+// window block.
+//
+// Why a second kernel.  With grouped query heads (Hq / Hkv = G > 1) a KV
+// head's keys are shared by G x W query rows, and the attention becomes
+// compute-bound; the kernel in attn_bf16.hip gives each K/V tile it loads to
+// 64 query rows, which leaves the matrix cores waiting on the tile stream:
+// streaming tiles from L2 into LDS reaches roughly 60-100 GB/s per CU on
+// MI355X, while 64 rows per 32 KB tile would need ~150 GB/s per CU to keep
+// the MFMA pipes full.  Here one workgroup of eight waves gives every tile to
+// up to 256 query rows (the unit's rows, a multiple of 16 chosen by the
+// planner), so the same stream feeds up to 4x the MFMA work.
+//
+// Design (one workgroup = 8 waves = one work unit, one workgroup per CU):
+//  * The unit's 16-row query blocks are dealt to the waves round-robin
+//    (block b -> wave b mod 8), so a wave owns one or two blocks and the two
+//    waves that share a SIMD (w and w + 4) never hold more blocks between
+//    them than any other pair plus one.  Every wave runs over every key of
+//    the unit: it owns its rows' online-softmax state outright, and no join
+//    is needed.
+//  * Keys are processed in halves of 32, software-pipelined within a wave:
+//    while the matrix cores compute the scores of half h + 1, the vector
+//    units turn the scores of half h into probabilities; then half h's PV
+//    product.  The V^T fragments of a half are read from LDS before the
+//    scores of the next half are started, so their latency is covered.
+//  * K/V tiles of 64 keys go HBM -> LDS with the direct loads through a
+//    four-stage ring: two tiles stream in while one is computed, one barrier
+//    per tile.
+//  * Scores are computed transposed (S^T = K Q^T), so a lane holds one query
+//    and the keys of its column, which is the B-operand layout of the PV
+//    product O^T = V^T P^T; V^T is read with ds_read_b64_tr_b16 and the LDS
+//    rows are swizzled as in attn_bf16.hip (conflict-free for both reads).
+//  * Online softmax in base 2 with the lazily raised reference maximum and
+//    per-lane partial sums of attn_bf16.hip.
+//  * A unit covers all keys of its rows and writes O in bf16 and the LSE
+//    (the planner never cuts these launches' keys into ranges).
+//
+// Measured on MI355X (8 requests, 28 query / 4 KV heads, 2048 cached keys,
+// three window blocks of 64: 1344 query rows per KV head): 67-72 us against
+// 81-85 us for attn_bf16.hip.  What bounds it: per 64-key tile and SIMD, the
+// matrix work (3 blocks x 512 cycles), the softmax's vector work (v_exp_f32
+// runs at a quarter of the VALU rate; ~480 cycles per block) and the LDS
+// reads (K fragments go through ds_read_b128 at ~130 B/clock per CU, V^T
+// through ds_read_b64_tr_b16 at ~250) are of the same size.
+
+#include "attn_lds.h"
+
+namespace d2f {
+namespace {
+
+constexpr int kGqaWaves = kGqaThreads / 64;
+constexpr int kGqaStages = 4;
+
+// s_waitcnt immediate: vmcnt(v) and lgkmcnt(0) (expcnt not waited).
+constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
+
+template <int D>
+__global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs a) {
+  constexpr int RS = D * 2;              // LDS row bytes
+  constexpr int KSTEPS = D / 32;         // MFMA k-steps over head_dim
+  constexpr int DBLK = D / 16;           // 16-dim blocks of the output
+  constexpr int CPR = D / 8;             // 16-byte chunks per K/V row
+  constexpr int TILE = kKTile * RS;      // bytes per K (or V) tile
+  constexpr int RPB = 1024 / RS;         // rows per 1 KB direct-load block
+  constexpr int NBLK = TILE / 1024;      // 1 KB blocks per tensor per tile
+  constexpr int LPW = NBLK / kGqaWaves;  // blocks per wave per tensor per tile
+  static_assert(LPW >= 1 && LPW * kGqaWaves == NBLK, "8 waves cover a tile in 1 KB blocks");
+  constexpr int LOADS = 2 * LPW;         // direct loads per wave per tile
+  constexpr int SB = 2 * TILE;           // bytes per LDS stage: [K tile][V tile]
+  constexpr int NST = kGqaStages;
+
+  const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
+  const int ri = find_req(a, u);
+  const int rb = a.req[ri].b, P = a.req[ri].prefix, W = a.req[ri].win;
+  const int qtiles = a.req[ri].qtiles;
+  const int local = u - a.req[ri].unit_base;
+  const int qt = local % qtiles;
+  const int kvh = local / qtiles;
+  const int G = a.group, B = a.bsz;
+  const int rows = G * W;
+  const int R = a.qrows;  // query rows per unit (a multiple of 16)
+  const int r0 = qt * R;
+  const int k_end = unit_key_end(a, qt, R, P, W, G, B);  // last key any row sees
+  const int k_full = a.cache_only ? P : P + min(W, ((r0 / G) / B + 1) * B);  // every row sees
+  const int nct = cache_tiles(P);
+  const int n = nct + window_tiles(P, k_end);  // tiles of the unit (all its keys)
+
+  const size_t head_c = (((size_t)rb * a.hkv + kvh) * (size_t)a.cap + a.req[ri].key_off) * D;
+  const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
+  const __bf16* kc = (const __bf16*)a.kc + head_c;
+  const __bf16* vc = (const __bf16*)a.vc + head_c;
+  const __bf16* kw = (const __bf16*)a.kw + head_w;
+  const __bf16* vw = (const __bf16*)a.vw + head_w;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lc = lane & 15, lg = lane >> 4;
+  const int nblk = (min(R, rows - r0) + 15) >> 4;  // 16-row blocks with a valid row
+  const int nq = (wave < nblk) + (wave + kGqaWaves < nblk);  // this wave's blocks: 0, 1, 2
+
+  // Loader: wave w copies 1 KB blocks w, w + 8, ... of each of K and V; lane
+  // l of block j carries the 16 bytes that belong at LDS position (row
+  // RPB j + l / CPR, chunk l % CPR), i.e. global chunk (l % CPR) ^ swz(row).
+  // A tile's rows all come from the cache or all from the window, so the
+  // base pointers are uniform; rows past a partial tile's end re-read its
+  // last row (in bounds; the mask gives them zero weight).
+  auto issue = [&](auto J, int t) __attribute__((always_inline)) {
+    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>();
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
+    const bool in_cache = t < nct;
+    const size_t o = (size_t)(in_cache ? lo : lo - P) * D;
+    const char* kb = (const char*)((in_cache ? kc : kw) + o);
+    const char* vb = (const char*)((in_cache ? vc : vw) + o);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave + kGqaWaves * i;
+      const int row = RPB * blk + lane / CPR;
+      const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
+      load_kv16(a.remap, kb, off, sb + blk * 1024);
+      load_kv16(a.remap, vb, off, sb + TILE + blk * 1024);
+    }
+  };
+  // Workgroup barrier between phases: this wave's LDS reads have returned
+  // and at most `pending` tiles of its direct loads are still in flight (1:
+  // the tile requested last; 2: the last two).
+  auto barrier = [&](int pending) __attribute__((always_inline)) {
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LOADS));
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LOADS));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Tiles 0, 1 and 2 are requested before the queries are loaded.
+  if (0 < n) issue(ic<0>{}, 0);
+  if (1 < n) issue(ic<1>{}, 1);
+  if (2 < n) issue(ic<2>{}, 2);
+
+  // The wave's query rows: block qb is the unit's block wave + 8 qb; lane
+  // (lc, lg) holds row lc of it (MFMA column lc).
+  int my_i[2], my_h[2], my_lim[2];
+  bool row_ok[2];
+  bf16x8 qf[2][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = r0 + 16 * (wave + kGqaWaves * qb) + lc;
+    row_ok[qb] = qb < nq && row < r0 + R && row < rows;
+    my_i[qb] = row_ok[qb] ? row / G : 0;
+    my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
+    my_lim[qb] = a.cache_only ? P : P + min(W, (my_i[qb] / B + 1) * B);
+    if (row_ok[qb]) {
+      const __bf16* qp =
+          (const __bf16*)a.q + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = *(const bf16x8*)(qp + 32 * s + 8 * lg);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = bf16x8{};
+    }
+  }
+  // Retire the query loads and the first tiles here, so that no wait in the
+  // loop has to count them; the barrier publishes tile 0 (and 1, 2).
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  if (n > 0) barrier(0);
+
+  f32x4 o[DBLK][2];
+#pragma unroll
+  for (int d = 0; d < DBLK; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+  const float c2 = a.c2;
+  // The keys are processed in halves of 32 (half h: keys 32 (h & 1) ..
+  // 32 (h & 1) + 31 of tile h >> 1), software-pipelined within each wave:
+  // step h computes the scores of half h + 1 on the matrix cores while the
+  // vector units turn the scores of half h into probabilities, then adds
+  // half h's P V product, then masks half h + 1 and raises its reference
+  // maximum when needed.  Scores: key block kb (16 keys) x query block qb;
+  // lane (lc, lg) holds keys 16 kb + 4 lg + r of the half for query column
+  // lc.  Probabilities in the PV B-operand layout: k-slot 8 lg + 4 kb + r is
+  // key 16 kb + 4 lg + r of the half.
+  f32x4 sa[2][2], sb[2][2];  // scores of alternate halves: [kb][qb]
+  bf16x8 pf[2];              // probabilities of the half whose PV is next: [qb]
+
+  // An opaque zero makes the LDS addresses local to each use, so that they
+  // are recomputed instead of being kept for all four stages.
+  auto opaque_zero = [&]() __attribute__((always_inline)) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return z;
+  };
+  // S^T of half h (its tile in stage J) into s.
+  auto scores = [&](auto J, auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+    if constexpr (QB > 0) {
+      const char* Ks = stage_buf<decltype(J)::value, SB>() + opaque_zero();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * (h & 1) + 16 * kb + lc;
+        bf16x8 ka[KSTEPS];
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+          ka[st] = *(const bf16x8*)(Ks + row * RS + (((4 * st + lg) ^ swz<D>(row)) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < KSTEPS; ++st)
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st], qf[qb][st], s[kb][qb], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // Mask half h's scores where needed (a partial tile, a row's visible keys
+  // ending), then raise the reference maximum where a score exceeds it by
+  // more than kSlack: rescale O and l (lazily, as in attn_bf16.hip).
+  auto prepare = [&](auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+    if constexpr (QB > 0) {
+      int lo, nv;
+      tile_span(h >> 1, nct, P, k_end, lo, nv);
+      const int klo = lo + 32 * (h & 1), nvh = nv - 32 * (h & 1);
+      if (nvh < 32 || klo + 32 > k_full) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int lim = min(nvh, my_lim[qb] - klo);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * kb + 4 * lg + r >= lim) s[kb][qb][r] = kNegInf;
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        if (__any(mx * c2 > m_run[qb] + kSlack)) {
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float m_new = fmaxf(m_run[qb], mx * c2);
+          const float alpha =
+              (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+#pragma unroll
+          for (int d = 0; d < DBLK; ++d) o[d][qb] *= alpha;
+          l_run[qb] *= alpha;
+          m_run[qb] = m_new;
+        }
+      }
+    }
+  };
+  // Probabilities of a half from its scores s (sums kept per lane).
+  auto probs = [&](auto QBc, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -m_use));
+          ps += p;
+          pf[qb][4 * kb + r] = (__bf16)p;
+        }
+      }
+      l_run[qb] += ps;
+    }
+  };
+  // V^T fragments of half h (its tile in stage J): lane (lc, lg) of a
+  // transposed read gets V[key 4 lg + e][dim 16 d + lc] of the half (e < 4),
+  // and 16 keys on from the second read, i.e. k-slots 8 lg .. 8 lg + 7 in
+  // the probabilities' key order.  They are read before the scores of the
+  // next half are computed, so that their latency is covered.
+  auto vload = [&](auto J, auto QBc, int h, bf16x8 (&va)[DBLK]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+    if constexpr (QB > 0) {
+      const lds_char* Vs =
+          (const lds_char*)(stage_buf<decltype(J)::value, SB>() + TILE + opaque_zero());
+      const int vr = 32 * (h & 1) + 4 * lg + (lc >> 2);
+      const int vbyte = (lc & 1) << 3;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) {
+        const int cidx = 2 * d + ((lc & 3) >> 1);
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + vr * RS + ((cidx ^ swz<D>(vr)) << 4) + vbyte));
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + (vr + 16) * RS + ((cidx ^ swz<D>(vr + 16)) << 4) + vbyte));
+        const i16x8 both = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+        va[d] = __builtin_bit_cast(bf16x8, both);
+      }
+    }
+  };
+  // O^T += V^T P^T with the fragments of vload.
+  auto pv = [&](auto QBc, const bf16x8 (&va)[DBLK]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[d][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[d], pf[qb], o[d][qb], 0, 0, 0);
+  };
+
+  // Tile t sits in stage t mod 4.  Step 2t (half 0 of tile t) reads only
+  // tile t.  Step 2t + 1 reads tile t (V of half 1) and tile t + 1 (K of its
+  // half 0): it starts with a barrier after which tile t + 1 is in LDS (this
+  // wave waits for its own loads of it; tile t + 2 may stay in flight) and
+  // every wave is past step 2t - 1, the last to read tile t - 1, whose stage
+  // then receives tile t + 3.
+  auto run = [&](auto QBc) __attribute__((always_inline)) {
+    scores(ic<0>{}, QBc, 0, sa);
+    prepare(QBc, 0, sa);
+    auto tile = [&](auto J, int t) __attribute__((always_inline)) {
+      constexpr int JK = decltype(J)::value;
+      bf16x8 va[DBLK];
+      // step 2t: scores of half 1 (same tile) while half 0 becomes P.
+      vload(J, QBc, 2 * t, va);
+      scores(J, QBc, 2 * t + 1, sb);
+      probs(QBc, sa);
+      pv(QBc, va);
+      prepare(QBc, 2 * t + 1, sb);
+      // step 2t + 1: the next tile's first half.
+      barrier(t + 2 < n ? 1 : 0);
+      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
+      vload(J, QBc, 2 * t + 1, va);
+      if (t + 1 < n) scores(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2, sa);
+      probs(QBc, sb);
+      pv(QBc, va);
+      if (t + 1 < n) prepare(QBc, 2 * t + 2, sa);
+    };
+    for (int t = 0; t < n; t += NST) {
+      tile(ic<0>{}, t);
+      if (t + 1 < n) tile(ic<1>{}, t + 1);
+      if (t + 2 < n) tile(ic<2>{}, t + 2);
+      if (t + 3 < n) tile(ic<3>{}, t + 3);
+    }
+  };
+  if (n > 0) {
+    if (nq == 2) run(ic<2>{});
+    else if (nq == 1) run(ic<1>{});
+    else run(ic<0>{});
+  }
+
+  // Per-lane partial sums to per-query sums (the 4 lanes of a query column),
+  // then the rows' outputs.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    l_run[qb] += __shfl_xor(l_run[qb], 16);
+    l_run[qb] += __shfl_xor(l_run[qb], 32);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!row_ok[qb]) continue;
+    const float inv = 1.0f / l_run[qb];
+    __bf16* op = (__bf16*)a.out + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) {
+      bf16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (__bf16)(o[d][qb][r] * inv);
+      *(bf16x4*)(op + 16 * d + 4 * lg) = v;
+    }
+    if (a.lse != nullptr && lg == 0)
+      a.lse[((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]] =
+          (m_run[qb] + log2f(l_run[qb])) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, hipStream_t s) {
+  const dim3 grid(a.n_units), block(kGqaThreads);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_gqa_kernel<128>), grid, block, 0, s, a);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL((attn_gqa_kernel<64>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace d2f

@@ -33,8 +33,9 @@ __device__ void merge_rows(const AttnArgs& a, int ri, int kvh, int qt, int row0)
   const int row = qt * a.qrows + r;
   if (r >= a.qrows || row >= G * W) return;
   const int i = row / G, h = kvh * G + row % G;
-  const size_t slot0 = ((size_t)(a.req[ri].unit_base + kvh * nsplit * qtiles + qt)) * kQTile + r;
-  const size_t sstride = (size_t)qtiles * kQTile;  // slot distance between splits
+  const size_t slot0 =
+      ((size_t)(a.req[ri].unit_base + kvh * nsplit * qtiles + qt)) * a.slot_rows + r;
+  const size_t sstride = (size_t)qtiles * a.slot_rows;  // slot distance between splits
 
   // Splits are taken kBatch at a time with all their loads in flight; a
   // batch raises the running max and rescales what was accumulated before.

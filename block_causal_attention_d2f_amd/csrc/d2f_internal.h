@@ -18,6 +18,8 @@ constexpr int kQTile = 64;   // query rows per workgroup
 constexpr int kKTile = 64;   // keys per K/V tile
 constexpr int kMaxReqPerLaunch = 64;
 constexpr int kAttnThreads = 256;
+constexpr int kGqaThreads = 512;   // grouped-query kernel (attn_gqa.hip): 8 waves
+constexpr int kGqaMaxRows = 256;   // its query rows per unit: 16 per block, <= 2 blocks per wave
 
 struct ReqInfo {
   int32_t b;          // batch index of the request
@@ -38,13 +40,14 @@ struct AttnArgs {
   const void* vw;
   void* out;
   float* lse;
-  float* ws_o;   // [unit][kQTile][D] unnormalised partial outputs
-  float* ws_ml;  // [unit][kQTile][2] running max (log2 units) and sum
+  float* ws_o;   // [unit][slot_rows][D] unnormalised partial outputs
+  float* ws_ml;  // [unit][slot_rows][2] running max (log2 units) and sum
   int64_t cap;   // cache slots per (request, KV head)
   int32_t hq, hkv, group, wmax, bsz;
   int32_t n_req, n_units, n_groups;
   int32_t remap;  // 1: keep a request's query tiles on one XCD (xcd_remap)
-  int32_t qrows;  // query rows per unit: kQTile, or 32 (bf16, narrow windows)
+  int32_t qrows;  // query rows per unit: kQTile, 32 (bf16, narrow windows) or the GQA kernel's
+  int32_t slot_rows;  // partial-result rows per unit in the workspace (>= qrows)
   int32_t cache_only;  // key-range calls: the keys are cache rows [key_off, key_off + prefix)
   int32_t wide;   // bf16: 1 = eight-wave workgroups, two tile groups
   float c2;       // softmax scale * log2(e)
@@ -125,6 +128,7 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool paged, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, hipStream_t s);
 // Attention workgroups that fit on one CU at once (0 if unknown).
 int attn_bf16_wgs_per_cu(int head_dim);
 int attn_f32_wgs_per_cu(int head_dim);
