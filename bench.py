@@ -131,6 +131,9 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="turn a rocprofv3 --pmc output dir with the MFMA counters of a bench "
                          "run of --config into profiles/mfma_<config>.txt; needs no GPU")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/kernel_trace_<config>.md from a rocprofv3 --kernel-trace "
+                         "--stats output directory")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE",
                                                               "RUN_FETCH", "RUN_WRITE"),
                     help="turn four rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of "
@@ -178,9 +181,8 @@ def _counter_means(d, counter):
     return {k: sums[k] / counts[k] for k in sums}
 
 
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
-                 "GRBM_GUI_ACTIVE")
-N_CU, SIMD_PER_CU, N_XCD = 256, 4, 8
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+                 "SQ_INSTS_VALU_TRANS_F32", "SQ_VALU_MFMA_BUSY_CYCLES")
 
 
 def _dispatch_ns(d, counter, name_part):
@@ -198,7 +200,7 @@ def _dispatch_ns(d, counter, name_part):
 
 
 def summarize_mfma(args):
-    """MFMA work and busy cycles of the attention kernel from counters."""
+    """Instruction mix and MFMA work of the attention kernels from counters."""
     import workloads as W
     d = args.summarize_mfma
     vals = {c: _counter_means(d, c) for c in MFMA_COUNTERS}
@@ -211,29 +213,38 @@ def summarize_mfma(args):
         short = name.replace("(anonymous namespace)::", "").split("(")[0]
         short = short.replace("void ", "").replace("d2f::", "")
         ns = _dispatch_ns(d, MFMA_COUNTERS[0], short.split("<")[0])
-        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"].get(name, 0.0)
-        gui = vals["GRBM_GUI_ACTIVE"].get(name, 0.0)
         flops = mops * 512.0
+        mfma = vals["SQ_INSTS_MFMA"].get(name, 0.0)
+        valu = vals["SQ_INSTS_VALU"].get(name, 0.0)
+        lds = vals["SQ_INSTS_LDS"].get(name, 0.0)
+        trans = vals["SQ_INSTS_VALU_TRANS_F32"].get(name, 0.0)
+        busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"].get(name, 0.0)
         kernels[short] = {
             "mfma_mops_bf16": round(mops), "mfma_flops": flops,
             "algorithmic_flops": flops_alg,
             "mfma_over_algorithmic": round(flops / flops_alg, 3),
-            "sq_valu_mfma_busy_cycles": round(busy), "sq_busy_cycles":
-                round(vals["SQ_BUSY_CYCLES"].get(name, 0.0)), "grbm_gui_active": round(gui),
-            "mfma_busy_frac": (round(busy / (gui / N_XCD * N_CU * SIMD_PER_CU), 4)
-                               if gui else None),
-            "clock_ghz_under_counters": round(gui / N_XCD / ns, 3) if gui and ns else None,
+            "sq_insts_mfma": round(mfma), "sq_insts_valu": round(valu),
+            "sq_insts_lds": round(lds), "sq_insts_valu_trans_f32": round(trans),
+            "valu_non_mfma_per_mfma": round((valu - mfma) / mfma, 3) if mfma else None,
+            "lds_per_mfma": round(lds / mfma, 3) if mfma else None,
+            "trans_per_mfma": round(trans / mfma, 3) if mfma else None,
+            "sq_valu_mfma_busy_cycles": round(busy),
+            "mfma_busy_cycles_per_mfma": round(busy / mfma, 2) if mfma else None,
             "avg_dispatch_us_under_counters": round(ns / 1e3, 3) if ns else None,
-            "mfma_tflops_under_counters": round(flops / ns / 1e3, 1) if ns else None}
+            "mfma_tflops_under_counters": round(flops / ns / 1e3, 1) if ns else None,
+            "frac_of_bf16_peak_under_counters":
+                round(flops / ns / 1e3 / PEAK_BF16_TFLOPS, 4) if ns else None}
     key = traffic_key(args)
     bs = "" if args.block_size is None else f" --block-size {args.block_size}"
-    hdr = (f"MFMA counters of the bf16 attention kernel, workload {key}.\n"
-           "Per-dispatch averages; mfma_flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;\n"
-           "GRBM_GUI_ACTIVE is summed over the 8 XCDs (per XCD it counts the kernel's clock\n"
-           "cycles: clock_ghz_under_counters), so mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES /\n"
-           "(GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs), the share of SIMD cycles with MFMA busy;\n"
-           "algorithmic_flops counts visible (query, key) pairs only (4 x head_dim each), so\n"
-           "mfma_over_algorithmic > 1 is padded rows and masked keys of partial tiles.\n"
+    hdr = (f"MFMA work and instruction mix of the bf16 attention kernels, workload {key}.\n"
+           "Per-dispatch averages (counters summed over the device).  mfma_flops =\n"
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; its rate over the dispatch time is the MFMA\n"
+           "utilisation against the 2500 TFLOP/s bf16 peak.  algorithmic_flops counts visible\n"
+           "(query, key) pairs only (4 x head_dim each), so mfma_over_algorithmic > 1 is padded\n"
+           "rows and masked keys of partial tiles.  SQ_INSTS_VALU includes the MFMA\n"
+           "instructions; the per-MFMA ratios give the vector, LDS and transcendental (exp)\n"
+           "instructions issued per v_mfma_f32_16x16x32_bf16.  SQ_VALU_MFMA_BUSY_CYCLES per\n"
+           "MFMA is the matrix core's occupancy per instruction (16 cycles at full rate).\n"
            "Command (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):\n"
            f"  rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d <dir> -- "
            f"python3 bench.py --config {args.config}{bs} --steps 2 --warmup 1 --call-reps 2 "
@@ -243,6 +254,45 @@ def summarize_mfma(args):
     with open(path, "w") as f:
         f.write(hdr + "\n---\n" + json.dumps({"config": key, "source_hash": kernel_source_hash(),
                                                 "kernels": kernels}, indent=1) + "\n")
+    print(path)
+
+
+def summarize_trace(args):
+    """Per-kernel durations of the library's kernels from a rocprofv3
+    --kernel-trace --stats run of this benchmark."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "d2f::" not in r["Name"]:
+                continue
+            short = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            short = short.replace("void ", "").replace("d2f::", "")
+            rows.append((short, int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"])))
+    rows.sort(key=lambda x: -x[1] * x[2])
+    key = traffic_key(args)
+    bs = "" if args.block_size is None else f" --block-size {args.block_size}"
+    extra = "".join(f" --{k.replace('_', '-')}" for k in ("paged", "round_prefix")
+                    if getattr(args, k, False))
+    lines = [f"# Kernel trace: {key}", "",
+             "Per-kernel durations of the library's kernels (rocprofv3 kernel trace; each",
+             "call of the benchmark's timed graphs, its per-call graphs and the eager spread",
+             "launches counted).", "",
+             "Command (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- \\",
+             f"        python3 bench.py --config {args.config}{bs}{extra} --steps 5 --warmup 2 "
+             "--no-cpu-baseline",
+             f"    python3 bench.py --config {args.config}{bs}{extra} --summarize-trace <dir>", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for short, calls, avg, mn, mx in rows:
+        lines.append(f"| {short} | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    lines += ["", f"source_hash: {kernel_source_hash()}", ""]
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{key}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
     print(path)
 
 
@@ -960,6 +1010,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

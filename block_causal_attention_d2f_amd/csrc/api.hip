@@ -50,6 +50,8 @@ constexpr double kSlotFill = 0.75;
 constexpr long long kSplitFactor = 2;
 constexpr int kDefaultCUs = 256;        // MI355X, used when no device is visible
 constexpr int kDefaultWgsPerCU = 2;
+constexpr long long kWideSplitMinTiles = 32;   // see plan_attention
+constexpr long long kWideSplitMaxTiles = 128;
 
 // Workgroups of the attention kernel resident at once on the current device.
 long long resident_workgroups(d2f_dtype_t dt, int head_dim) {
@@ -344,6 +346,37 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
                               (long long)(kSlotFill * (double)resident));
   if (d->dtype != D2F_BF16) return ws;
   const long long cus = device_cus();
+  // A split call with few, long key ranges (a long prefix over few heads)
+  // is re-planned for one eight-wave unit per CU, if that keeps every range
+  // between kWideSplitMinTiles and kWideSplitMaxTiles tiles.  Measured on
+  // MI355X, 32 heads over a 32768-token prefix: 8 ranges of 64 tiles on
+  // eight waves 92.8-95.9 us against 97.0-99.2 us for 12 ranges on four
+  // waves; with a 131072-token prefix (256-tile ranges) the four-wave plan
+  // stays faster (332 vs 350 us), and 512 tokens (3-tile ranges) too.
+  bool split = false;
+  for (const Launch& L : out) split |= L.any_split;
+  if (split && !paged) {
+    std::vector<Launch> wide;
+    const size_t ws2 = plan_pass(d, prefix, nwin, wide, key_off, kMinChunkTiles, cus);
+    const int G = d->n_heads_q / d->n_heads_kv;
+    bool ok = !wide.empty();
+    for (const Launch& L : wide) {
+      ok &= L.n_units <= cus;
+      for (const ReqInfo& r : L.req) {
+        const long long tiles = host_key_tiles(
+            r.prefix, key_off != nullptr ? r.prefix
+                                         : host_tile_key_end(r.qtiles - 1, L.qrows, r.prefix,
+                                                             r.win, G, d->block_size));
+        const long long len = (tiles + r.nsplit - 1) / r.nsplit;
+        ok &= r.nsplit > 1 && len >= kWideSplitMinTiles && len <= kWideSplitMaxTiles;
+      }
+    }
+    if (ok) {
+      for (Launch& L : wide) L.wide = true;
+      out = std::move(wide);
+      return ws2;
+    }
+  }
   for (const Launch& L : out)
     if (L.n_units > cus || L.any_split) return ws;
   for (Launch& L : out) L.wide = true;

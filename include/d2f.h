@@ -90,9 +90,10 @@ typedef struct {
   float softmax_scale;
 } d2f_attn_desc_t;
 
-/* Bytes of device workspace d2f_block_attn needs for these lengths (0 when
- * no key range is split), written to *bytes_out.  Same argument rules as
- * d2f_block_attn.  The size comes back through an out-parameter, with a
+/* Bytes of device workspace d2f_block_attn and d2f_block_attn_paged need for
+ * these lengths (0 when no key range is split), written to *bytes_out: the
+ * larger of the two calls' needs, so one size serves both.  Same argument
+ * rules as d2f_block_attn.  The size comes back through an out-parameter, with a
  * status as the return value, because 0 is a valid size (no split): a size
  * returned directly could not tell "nothing needed" from "invalid
  * arguments". */

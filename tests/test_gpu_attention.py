@@ -116,6 +116,17 @@ def test_llada_p32k():
     _check(sh, pairs=pairs, label="llada_p32k")
 
 
+def test_long_prefix_ranges_on_eight_waves():
+    """A 16384-token prefix over 32 heads: the plan cuts each head's keys into
+    8 ranges of ~33 tiles, one eight-wave unit per CU, merged exactly.
+    Sampled heads against the oracle; two runs bit-identical."""
+    shape = W.make_shape(1, 32, 32, 128, 16, [16384], [4], dtype="bf16")
+    x, out, lse, _ = _check(shape, seed=21, pairs=[(0, 0), (0, 13), (0, 31)],
+                            label="prefix16k-8ranges")
+    o2, l2 = run_attn(shape, x, out_fill=7.0)
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+
+
 def test_context_128k():
     """A 131072-token prefix (the pages' open question about 100K+ contexts):
     sampled heads against the oracle; every unread slot is NaN."""
