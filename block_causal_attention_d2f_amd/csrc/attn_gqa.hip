@@ -41,8 +41,12 @@
 //    (the planner never cuts these launches' keys into ranges).
 //
 // Measured on MI355X (8 requests, 28 query / 4 KV heads, 2048 cached keys,
-// three window blocks of 64: 1344 query rows per KV head): 67-72 us against
-// 81-85 us for attn_bf16.hip.  What bounds it: per 64-key tile and SIMD, the
+// three window blocks of 64: 1344 query rows per KV head): 70 us against 76
+// us for the first version of this kernel and 81-85 us for attn_bf16.hip on
+// the same machines.  Tried and slower: scheduling-group barriers that
+// interleave one MFMA with four vector instructions (81 us), a raised wave
+// priority while the scores' MFMAs issue (76 us), and LDS addresses
+// recomputed in every step to save registers (73 us).  What bounds it: per 64-key tile and SIMD, the
 // matrix work (3 blocks x 512 cycles), the softmax's vector work (v_exp_f32
 // runs at a quarter of the VALU rate; ~480 cycles per block) and the LDS
 // reads (K fragments go through ds_read_b128 at ~130 B/clock per CU, V^T
@@ -55,6 +59,7 @@ namespace {
 
 constexpr int kGqaWaves = kGqaThreads / 64;
 constexpr int kGqaStages = 4;
+constexpr float kSlackSum = 256.f;  // 2^kSlack: largest per-lane probability sum kept
 
 // s_waitcnt immediate: vmcnt(v) and lgkmcnt(0) (expcnt not waited).
 constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
@@ -173,7 +178,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   f32x4 o[DBLK][2];
 #pragma unroll
   for (int d = 0; d < DBLK; ++d) o[d][0] = o[d][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+  // Reference maxima start at the finite sentinel -FLT_MAX (see probs).
+  float m_run[2] = {-__FLT_MAX__, -__FLT_MAX__}, l_run[2] = {0.f, 0.f};
   const float c2 = a.c2;
   // The keys are processed in halves of 32 (half h: keys 32 (h & 1) ..
   // 32 (h & 1) + 31 of tile h >> 1), software-pipelined within each wave:
@@ -187,18 +193,11 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   f32x4 sa[2][2], sb[2][2];  // scores of alternate halves: [kb][qb]
   bf16x8 pf[2];              // probabilities of the half whose PV is next: [qb]
 
-  // An opaque zero makes the LDS addresses local to each use, so that they
-  // are recomputed instead of being kept for all four stages.
-  auto opaque_zero = [&]() __attribute__((always_inline)) {
-    int z = 0;
-    asm volatile("" : "+v"(z));
-    return z;
-  };
   // S^T of half h (its tile in stage J) into s.
   auto scores = [&](auto J, auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
-      const char* Ks = stage_buf<decltype(J)::value, SB>() + opaque_zero();
+      const char* Ks = stage_buf<decltype(J)::value, SB>();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = 32 * (h & 1) + 16 * kb + lc;
@@ -217,8 +216,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     }
   };
   // Mask half h's scores where needed (a partial tile, a row's visible keys
-  // ending), then raise the reference maximum where a score exceeds it by
-  // more than kSlack: rescale O and l (lazily, as in attn_bf16.hip).
+  // ending).
   auto prepare = [&](auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
@@ -236,44 +234,60 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
               if (16 * kb + 4 * lg + r >= lim) s[kb][qb][r] = kNegInf;
         }
       }
+    }
+  };
+  // Probabilities of a half from its scores s against the reference maximum
+  // m_run (base-2 units), in straight-line code; a lane's sum ps bounds each
+  // of its probabilities.  Only when some lane's sum exceeds 2^kSlack (so a
+  // probability may have) -- and on the first half, where m_run is still the
+  // finite sentinel -FLT_MAX and every visible score gives +inf -- is the
+  // reference raised to the half's true maximum, O and l rescaled and the
+  // probabilities recomputed.  The reference only moves to maxima actually
+  // seen, so the row's largest score keeps a probability >= 1.
+  auto probs = [&](auto QBc, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+    float ps[QB > 0 ? QB : 1];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
+      ps[qb] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -m_run[qb]));
+          ps[qb] += p;
+          pf[qb][4 * kb + r] = (__bf16)p;
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__any(!(ps[qb] <= kSlackSum))) {
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        if (__any(mx * c2 > m_run[qb] + kSlack)) {
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float m_new = fmaxf(m_run[qb], mx * c2);
-          const float alpha =
-              (m_run[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx * c2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
 #pragma unroll
-          for (int d = 0; d < DBLK; ++d) o[d][qb] *= alpha;
-          l_run[qb] *= alpha;
-          m_run[qb] = m_new;
+        for (int d = 0; d < DBLK; ++d) o[d][qb] *= alpha;
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+        ps[qb] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -m_new));
+            ps[qb] += p;
+            pf[qb][4 * kb + r] = (__bf16)p;
+          }
         }
       }
-    }
-  };
-  // Probabilities of a half from its scores s (sums kept per lane).
-  auto probs = [&](auto QBc, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
-    constexpr int QB = decltype(QBc)::value;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_use = (m_run[qb] == kNegInf) ? 0.f : m_run[qb];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, -m_use));
-          ps += p;
-          pf[qb][4 * kb + r] = (__bf16)p;
-        }
-      }
-      l_run[qb] += ps;
+      l_run[qb] += ps[qb];
     }
   };
   // V^T fragments of half h (its tile in stage J): lane (lc, lg) of a
@@ -285,7 +299,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
       const lds_char* Vs =
-          (const lds_char*)(stage_buf<decltype(J)::value, SB>() + TILE + opaque_zero());
+          (const lds_char*)(stage_buf<decltype(J)::value, SB>() + TILE);
       const int vr = 32 * (h & 1) + 4 * lg + (lc >> 2);
       const int vbyte = (lc & 1) << 3;
 #pragma unroll
