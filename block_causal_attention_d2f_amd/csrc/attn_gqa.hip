@@ -41,12 +41,18 @@
 //    (the planner never cuts these launches' keys into ranges).
 //
 // Measured on MI355X (8 requests, 28 query / 4 KV heads, 2048 cached keys,
-// three window blocks of 64: 1344 query rows per KV head): 70 us against 76
-// us for the first version of this kernel and 81-85 us for attn_bf16.hip on
-// the same machines.  Tried and slower: scheduling-group barriers that
-// interleave one MFMA with four vector instructions (81 us), a raised wave
-// priority while the scores' MFMAs issue (76 us), and LDS addresses
-// recomputed in every step to save registers (73 us).  What bounds it: per 64-key tile and SIMD, the
+// three window blocks of 64: 1344 query rows per KV head): 66-70 us against
+// 76 us for the first version of this kernel and 81-85 us for attn_bf16.hip
+// on the same machines.  Tried and not faster: scheduling-group barriers
+// that interleave one MFMA with four vector instructions (81 us), a raised
+// wave priority while the scores' MFMAs issue (76 us), LDS addresses
+// recomputed in every step to save registers (73 us), a ring of three or
+// five tiles (within noise), the V^T reads after the scores' MFMAs instead
+// of between the K reads and them (+3%), and two groups of four waves that
+// split each tile's keys and join through LDS at the end, which halves the
+// LDS reads per tile (no gain at 48 to 128 rows per unit).  Cutting the keys
+// into ranges merged by attn_merge.hip lost to the merge pass at every
+// size tried.  What bounds it: per 64-key tile and SIMD, the
 // matrix work (3 blocks x 512 cycles), the softmax's vector work (v_exp_f32
 // runs at a quarter of the VALU rate; ~480 cycles per block) and the LDS
 // reads (K fragments go through ds_read_b128 at ~130 B/clock per CU, V^T
@@ -193,27 +199,33 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   f32x4 sa[2][2], sb[2][2];  // scores of alternate halves: [kb][qb]
   bf16x8 pf[2];              // probabilities of the half whose PV is next: [qb]
 
-  // S^T of half h (its tile in stage J) into s.
-  auto scores = [&](auto J, auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
+  // K fragments of half h (its tile in stage J): key block kb, k-step st.
+  auto kread = [&](auto J, auto QBc, int h, bf16x8 (&ka)[2][KSTEPS]) __attribute__((always_inline)) {
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
       const char* Ks = stage_buf<decltype(J)::value, SB>();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = 32 * (h & 1) + 16 * kb + lc;
-        bf16x8 ka[KSTEPS];
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st)
-          ka[st] = *(const bf16x8*)(Ks + row * RS + (((4 * st + lg) ^ swz<D>(row)) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < KSTEPS; ++st)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st], qf[qb][st], s[kb][qb], 0, 0, 0);
-        }
+          ka[kb][st] = *(const bf16x8*)(Ks + row * RS + (((4 * st + lg) ^ swz<D>(row)) << 4));
       }
     }
+  };
+  // S^T of a half from its K fragments into s.
+  auto smma = [&](auto QBc, const bf16x8 (&ka)[2][KSTEPS], f32x4 (&s)[2][2])
+      __attribute__((always_inline)) {
+    constexpr int QB = decltype(QBc)::value;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][st], qf[qb][st], s[kb][qb], 0, 0, 0);
+      }
   };
   // Mask half h's scores where needed (a partial tile, a row's visible keys
   // ending).
@@ -293,8 +305,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // V^T fragments of half h (its tile in stage J): lane (lc, lg) of a
   // transposed read gets V[key 4 lg + e][dim 16 d + lc] of the half (e < 4),
   // and 16 keys on from the second read, i.e. k-slots 8 lg .. 8 lg + 7 in
-  // the probabilities' key order.  They are read before the scores of the
-  // next half are computed, so that their latency is covered.
+  // the probabilities' key order.
   auto vload = [&](auto J, auto QBc, int h, bf16x8 (&va)[DBLK]) __attribute__((always_inline)) {
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
@@ -330,23 +341,40 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // wave waits for its own loads of it; tile t + 2 may stay in flight) and
   // every wave is past step 2t - 1, the last to read tile t - 1, whose stage
   // then receives tile t + 3.
+  // Within a step the K fragments of the next half are requested before
+  // the V^T fragments of this one: LDS returns reads in order, and the
+  // scores' MFMAs, which come first, then wait only for the K reads.
   auto run = [&](auto QBc) __attribute__((always_inline)) {
-    scores(ic<0>{}, QBc, 0, sa);
+    {
+      bf16x8 ka[2][KSTEPS];
+      kread(ic<0>{}, QBc, 0, ka);
+      smma(QBc, ka, sa);
+    }
     prepare(QBc, 0, sa);
     auto tile = [&](auto J, int t) __attribute__((always_inline)) {
       constexpr int JK = decltype(J)::value;
       bf16x8 va[DBLK];
       // step 2t: scores of half 1 (same tile) while half 0 becomes P.
-      vload(J, QBc, 2 * t, va);
-      scores(J, QBc, 2 * t + 1, sb);
+      {
+        bf16x8 ka[2][KSTEPS];
+        kread(J, QBc, 2 * t + 1, ka);
+        vload(J, QBc, 2 * t, va);
+        smma(QBc, ka, sb);
+      }
       probs(QBc, sa);
       pv(QBc, va);
       prepare(QBc, 2 * t + 1, sb);
       // step 2t + 1: the next tile's first half.
       barrier(t + 2 < n ? 1 : 0);
       if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
-      vload(J, QBc, 2 * t + 1, va);
-      if (t + 1 < n) scores(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2, sa);
+      if (t + 1 < n) {
+        bf16x8 ka[2][KSTEPS];
+        kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2, ka);
+        vload(J, QBc, 2 * t + 1, va);
+        smma(QBc, ka, sa);
+      } else {
+        vload(J, QBc, 2 * t + 1, va);
+      }
       probs(QBc, sb);
       pv(QBc, va);
       if (t + 1 < n) prepare(QBc, 2 * t + 2, sa);

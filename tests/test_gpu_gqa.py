@@ -2,7 +2,7 @@
 fp64 oracle, through the C ABI.
 
 The library sends a bf16 call there when the query heads share KV heads and
-the call has at least 128 query rows per compute unit (32768 rows on the
+the call has at least 64 query rows per compute unit (16384 rows on the
 256-CU MI355X); every shape below is above that.  The draws vary batch, KV
 heads, group size, head_dim, block size and window, with prefixes that mix
 tile-boundary lengths (0, 1, 63, 64, 65) and uniform ones; unread cache
@@ -16,7 +16,7 @@ from parity import compare_attn, oracle_attn, poisoned_inputs, run_attn, say
 
 pytestmark = pytest.mark.gpu
 
-MIN_ROWS = 128 * 256  # query rows that route a grouped-query bf16 call to the kernel
+MIN_ROWS = 64 * 256  # query rows that route a grouped-query bf16 call to the kernel
 
 
 def _rows(sh):
@@ -73,6 +73,7 @@ def test_random_gqa_shapes(k):
     (11, 12, 4, 64, 64, [129 * i for i in range(11)], [4] * 11),       # group 3, head_dim 64
     (16, 64, 8, 128, 8, [7 * i * i for i in range(16)], [4] * 16),      # B = 8: 4 blocks per tile
     (2, 128, 8, 128, 48, [0, 777], [3, 3]),                              # group 16, B = 48
+    (8, 28, 4, 128, 32, [2048, 2047, 1, 64, 65, 0, 1500, 2048], [3] * 8), # Dream shape, B = 32
 ])
 def test_gqa_edge_shapes(case):
     nb, hq, hkv, d, b, prefix, nwin = case
