@@ -23,9 +23,9 @@
 // shuffles, then a fixed-order cross-wave step), and the threads holding the
 // maximum agree on its first index.  COMMITTED rows are not read.
 //
-// Kernel 2 (commit_decide): one workgroup per D2F block.  A thread per row
-// merges the row's chunk partials (loads in flight together, folded in chunk
-// order), conf = 1 / sum (the max term is exp(0) = 1) is
+// Kernel 2 (commit_decide): one workgroup per D2F block.  A group of lanes
+// per row merges the row's chunk partials (all loads in flight together, a
+// fixed merge order), conf = 1 / sum (the max term is exp(0) = 1) is
 // compared with the threshold, the aggressive top-k ranks the block's masked
 // rows (ties to the lower position), and the new mask state, tokens and
 // per-block counts are written.  No floating-point atomics: results are
@@ -228,32 +228,49 @@ __device__ void reduce_chunk(const CommitArgs& a, int row, int ck, float4& resul
 
 // Combine the chunk partials of every row of one block into s_conf / s_idx
 // (and s_gap, the logit gap, when AUX is the second-largest value) and mark
-// the MASKED rows in s_live: one thread per row loads kBatch partials at a
-// time, all in flight, and folds them in chunk order (a fixed order: the
-// result does not depend on timing).
+// the MASKED rows in s_live.  A row's chunks go to a group of L lanes of one
+// wave (L the largest power of two, at most 64, with B L <= the workgroup's
+// threads): lane j of the group loads chunks j, j + L, ..., kBatch at a time
+// all in flight, and folds them in chunk order; the group then merges its
+// lanes' partials in a fixed butterfly (exchange partner j ^ 1, then j ^ 2,
+// ...), and since the merge is symmetric every lane ends with the same
+// result.  The order is fixed, so the result does not depend on timing.
 // The loads do not wait for the mask state: a row that is not MASKED has no
 // partials written, and what is read for it is discarded.
 template <int AUX>
 __device__ void combine_rows(const CommitArgs& a, size_t row0, int B, float* s_conf, int* s_idx,
                              float* s_gap, unsigned char* s_live) {
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 8;
   constexpr float kX0 = AUX == kAuxSecond ? kNegInf : 0.f;
   const int nck = a.n_chunks;
-  for (int p = threadIdx.x; p < B; p += kCommitThreads) {
-    const bool live = a.mask_state[row0 + p] == D2F_MASKED;
-    const float4* src = a.partial + (row0 + p) * nck;
+  int L = 1;
+  while (L < 64 && 2 * L * B <= kCommitThreads) L *= 2;
+  const int rows_per_pass = kCommitThreads / L;
+  const int j = (int)threadIdx.x % L;
+  for (int p0 = 0; p0 < B; p0 += rows_per_pass) {
+    const int p = p0 + (int)threadIdx.x / L;
+    const bool in_block = p < B;
+    const bool live = in_block && a.mask_state[row0 + p] == D2F_MASKED;
     float m = kNegInf, sm = 0.f, xa = kX0;
     int ix = INT_MAX;
-    for (int c0 = 0; c0 < nck; c0 += kBatch) {
-      float4 v[kBatch];
+    if (in_block) {
+      const float4* src = a.partial + (row0 + p) * nck;
+      for (int c0 = j; c0 < nck; c0 += kBatch * L) {
+        float4 v[kBatch];
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        v[k] = (c0 + k < nck) ? src[c0 + k]
-                              : make_float4(kNegInf, 0.f, __int_as_float(INT_MAX), kX0);
+        for (int k = 0; k < kBatch; ++k) {
+          const int c = c0 + k * L;
+          v[k] = c < nck ? src[c] : make_float4(kNegInf, 0.f, __int_as_float(INT_MAX), kX0);
+        }
 #pragma unroll
-      for (int k = 0; k < kBatch; ++k)
-        combine<AUX>(m, sm, ix, xa, v[k].x, v[k].y, __float_as_int(v[k].z), v[k].w);
+        for (int k = 0; k < kBatch; ++k)
+          combine<AUX>(m, sm, ix, xa, v[k].x, v[k].y, __float_as_int(v[k].z), v[k].w);
+      }
     }
+    for (int o = 1; o < L; o <<= 1)
+      combine<AUX>(m, sm, ix, xa, __shfl_xor(m, o), __shfl_xor(sm, o), __shfl_xor(ix, o),
+                   __shfl_xor(xa, o));
+    if (!in_block || j != 0) continue;
     float c = 1.0f / sm;  // maximum probability: the max term is exp(0) = 1
     if (AUX == kAuxSecond) {
       const float gap = m - xa;  // >= 0; +inf when the row has one entry
