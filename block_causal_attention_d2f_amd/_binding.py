@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libd2f.so")
+# D2F_LIB selects another build of the library (the host-sanitized one).
+LIB_PATH = os.environ.get("D2F_LIB") or os.path.join(_PKG, "libd2f.so")
 
 D2F_OK = 0
 STATUS_NAMES = {0: "D2F_OK", 1: "D2F_ERR_INVALID_ARG", 2: "D2F_ERR_CAPACITY",
