@@ -165,6 +165,37 @@ CALL_OF_KERNEL = (("attn_bf16_kernel", "d2f_block_attn"), ("attn_gqa_kernel", "d
                   ("kv_commit_kernel", "d2f_kv_commit"))
 
 
+def kernel_short_name(name):
+    """Readable name of one of the library's kernels as rocprofv3 reports it:
+    demangled ("void d2f::(anonymous namespace)::k<128, 2>(d2f::AttnArgs)"),
+    or left mangled when it could not demangle a template argument (it leaves
+    __bf16, mangled DF16b, alone).  None for other kernels."""
+    import re
+    if "d2f::" in name:
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        return short.replace("void ", "").replace("d2f::", "")
+    m = re.match(r"_ZN3d2f(?:\d+_GLOBAL__N_1)?(\d+)", name)
+    if not m:
+        return None
+    n = int(m.group(1))
+    ident = name[m.end():m.end() + n]
+    rest = name[m.end() + n:]
+    args = []
+    if rest.startswith("I"):
+        tok = re.compile(r"Li(-?\d+)E|Lb([01])E|DF16b|f|d")
+        i = 1
+        while i < len(rest) and rest[i] != "E":
+            t = tok.match(rest, i)
+            if not t:
+                break
+            g = t.group(0)
+            args.append(t.group(1) if t.group(1) is not None else
+                        ("true" if t.group(2) == "1" else "false") if t.group(2) is not None else
+                        {"DF16b": "__bf16", "f": "float", "d": "double"}[g])
+            i = t.end()
+    return ident + (f"<{', '.join(args)}>" if args else "")
+
+
 def _counter_means(d, counter):
     """Average per-dispatch value of `counter` for each kernel in a rocprofv3
     --pmc csv output directory."""
@@ -210,8 +241,7 @@ def summarize_mfma(args):
     for name, mops in vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"].items():
         if "attn_bf16_kernel" not in name and "attn_gqa_kernel" not in name:
             continue
-        short = name.replace("(anonymous namespace)::", "").split("(")[0]
-        short = short.replace("void ", "").replace("d2f::", "")
+        short = kernel_short_name(name) or name[:60]
         ns = _dispatch_ns(d, MFMA_COUNTERS[0], short.split("<")[0])
         flops = mops * 512.0
         mfma = vals["SQ_INSTS_MFMA"].get(name, 0.0)
@@ -266,26 +296,32 @@ def summarize_trace(args):
     rows = []
     for f in files:
         for r in csv.DictReader(open(f)):
-            if "d2f::" not in r["Name"]:
+            short = kernel_short_name(r["Name"])
+            if short is None:
                 continue
-            short = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
-            short = short.replace("void ", "").replace("d2f::", "")
             rows.append((short, int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
                          float(r["MaxNs"])))
     rows.sort(key=lambda x: -x[1] * x[2])
-    key = traffic_key(args)
-    bs = "" if args.block_size is None else f" --block-size {args.block_size}"
-    extra = "".join(f" --{k.replace('_', '-')}" for k in ("paged", "round_prefix")
-                    if getattr(args, k, False))
-    lines = [f"# Kernel trace: {key}", "",
-             "Per-kernel durations of the library's kernels (rocprofv3 kernel trace; each",
-             "call of the benchmark's timed graphs, its per-call graphs and the eager spread",
-             "launches counted).", "",
+    if args.decode_loop:
+        key = "decode_loop_llada_batched"
+        run = "--decode-loop --loop-reps 1"
+        what = ["Per-kernel durations of the library's kernels over the pipelined decoding",
+                "loop (bench.py --decode-loop: one warm-up, one timed and one phase-timed decode",
+                "of the batched ragged LLaDA-8B-shaped workload; rocprofv3 kernel trace)."]
+    else:
+        key = traffic_key(args)
+        bs = "" if args.block_size is None else f" --block-size {args.block_size}"
+        extra = "".join(f" --{k.replace('_', '-')}" for k in ("paged", "round_prefix")
+                        if getattr(args, k, False))
+        run = f"--config {args.config}{bs}{extra} --steps 5 --warmup 2 --no-cpu-baseline"
+        what = ["Per-kernel durations of the library's kernels (rocprofv3 kernel trace; each",
+                "call of the benchmark's timed graphs, its per-call graphs and the eager spread",
+                "launches counted)."]
+    lines = [f"# Kernel trace: {key}", "", *what, "",
              "Command (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o kt -- \\",
-             f"        python3 bench.py --config {args.config}{bs}{extra} --steps 5 --warmup 2 "
-             "--no-cpu-baseline",
-             f"    python3 bench.py --config {args.config}{bs}{extra} --summarize-trace <dir>", "",
+             f"        python3 bench.py {run}",
+             f"    python3 bench.py {run.split(' --steps')[0]} --summarize-trace <dir>", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
     for short, calls, avg, mn, mx in rows:
         lines.append(f"| {short} | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
@@ -312,8 +348,7 @@ def summarize_counters(args):
         e = calls.setdefault(call, {"kernels": {}, "bytes_per_call": 0.0})
         fb = rf[name] * 1024 * f_fetch
         wb = rw.get(name, 0.0) * 1024 * f_write
-        short = name.replace("(anonymous namespace)::", "").split("(")[0]
-        short = short.replace("void ", "").replace("d2f::", "")
+        short = kernel_short_name(name) or name[:60]
         e["kernels"][short] = {"fetch_kib": round(rf[name], 1),
                                                   "write_kib": round(rw.get(name, 0.0), 1),
                                                   "bytes": round(fb + wb)}

@@ -77,3 +77,17 @@ def test_input_sets_budget_caps_the_per_call_rule():
     # per-call rule asks for 1 + ceil(640 / 1) = 641 sets; 1 GB sets cap it at 64
     n = bench.input_set_count(2_000 * MB, 1 * MB, 1 << 30)
     assert n == bench.SET_BUDGET_BYTES // (1 << 30)
+
+
+def test_kernel_short_name_reads_mangled_and_demangled_names():
+    import bench
+    assert bench.kernel_short_name(
+        "_ZN3d2f12_GLOBAL__N_117attn_merge_kernelILi128EDF16bEEvNS_8AttnArgsE") == \
+        "attn_merge_kernel<128, __bf16>"
+    assert bench.kernel_short_name(
+        "void d2f::(anonymous namespace)::attn_bf16_kernel<128, 2, 0, 2>(d2f::AttnArgs)") == \
+        "attn_bf16_kernel<128, 2, 0, 2>"
+    assert bench.kernel_short_name(
+        "_ZN3d2f12_GLOBAL__N_119vocab_reduce_kernelILb1ELi0EEEvNS_10CommitArgsE") == \
+        "vocab_reduce_kernel<true, 0>"
+    assert bench.kernel_short_name("void at::native::fill_kernel(int)") is None
