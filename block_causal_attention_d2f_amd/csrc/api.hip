@@ -249,10 +249,10 @@ size_t plan_pass(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t*
   return ws;
 }
 
-// Calls that go to the grouped-query kernel: bf16 grouped-query calls on a
-// contiguous cache (the paged loader is the four-wave kernel's) with at
-// least kGqaMinRowsPerCU query rows per CU over the call, where a unit per
-// CU gives each K/V tile enough rows.  Measured on MI355X with 28 query / 4
+// Calls that go to the grouped-query kernel: bf16 grouped-query calls (on a
+// contiguous or a paged cache: the plan does not depend on the layout, so
+// the two give the same bits) with at least kGqaMinRowsPerCU query rows per
+// CU over the call, where a unit per CU gives each K/V tile enough rows.  Measured on MI355X with 28 query / 4
 // KV heads, 8 requests and 2048 cached keys: 1344 rows per KV head (168 per
 // CU) 66-70 us against 81-85 us on the four-wave kernels; 672 rows (84 per
 // CU, 96-row units) 48.8 vs 51.6 us; 336 rows (42 per CU) 37.5 us with
@@ -340,7 +340,7 @@ size_t plan_gqa(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* 
 size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
                       std::vector<Launch>& out, const int32_t* key_off = nullptr,
                       bool paged = false) {
-  if (!paged && use_gqa(d, nwin, device_cus()))
+  if (use_gqa(d, nwin, device_cus()))
     return plan_gqa(d, prefix, nwin, out, key_off, device_cus());
   const long long resident = resident_workgroups(d->dtype, d->head_dim);
   const size_t ws = plan_pass(d, prefix, nwin, out, key_off, kMinChunkTiles,
@@ -467,7 +467,7 @@ d2f_status_t run_attention(const d2f_attn_desc_t* desc, const void* q, const voi
       a.page_shift = sh;
     }
     for (size_t i = 0; i < L.req.size(); ++i) a.req[i] = L.req[i];
-    hipError_t e = L.gqa ? launch_attn_gqa(a, desc->head_dim, s)
+    hipError_t e = L.gqa ? launch_attn_gqa(a, desc->head_dim, paged != nullptr, s)
                    : desc->dtype == D2F_BF16
                        ? launch_attn_bf16(a, desc->head_dim, paged != nullptr, s)
                        : launch_attn_f32(a, desc->head_dim, s);

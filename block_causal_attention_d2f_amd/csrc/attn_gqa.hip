@@ -70,7 +70,9 @@ constexpr float kSlackSum = 256.f;  // 2^kSlack: largest per-lane probability su
 // s_waitcnt immediate: vmcnt(v) and lgkmcnt(0) (expcnt not waited).
 constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
 
-template <int D>
+// PAGED: K/V rows are found through the page tables (AttnArgs), in pages of
+// a power of two >= 8 rows.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;              // LDS row bytes
   constexpr int KSTEPS = D / 32;         // MFMA k-steps over head_dim
@@ -120,7 +122,69 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // A tile's rows all come from the cache or all from the window, so the
   // base pointers are uniform; rows past a partial tile's end re-read its
   // last row (in bounds; the mask gives them zero weight).
+  // Paged loader: wave w copies the tile's consecutive blocks LPW w ..
+  // LPW w + LPW - 1, i.e. its rows 8 w .. 8 w + 7 (8 rows at either head
+  // dim), which start at a multiple of 8 of the cache or the window and so
+  // lie in one page: the load's base address stays uniform.  Rows past a
+  // partial tile's end re-read its last row, which lies in the same 8-row
+  // group or, for a group wholly past the end, is the group's only row.
+  // The wave's page of tile t: row group key0 of the cache or window, page
+  // index key0 >> shift, first row of that page relative to the tile.
+  static_assert(RPB * LPW == 8, "a wave loads 8 rows of a tile");
+  const size_t page_bytes = (size_t)a.hkv * B * D * sizeof(__bf16);
+  auto page_slot = [&](int t, const int32_t*& table, int& pi, int& row0)
+      __attribute__((always_inline)) {
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
+    const bool in_cache = t < nct;
+    const int r0 = in_cache ? lo : lo - P;  // first row's index in the cache or the window
+    table = in_cache ? a.page_table + (size_t)rb * a.table_stride
+                     : a.win_pages + (size_t)rb * (a.wmax / B);
+    const int key0 = r0 + min(RPB * LPW * wave, nv - 1);
+    pi = key0 >> a.page_shift;
+    row0 = (pi << a.page_shift) - r0;
+  };
+  // Table entries of 64 tiles at a time, one per lane (lane k: tile base +
+  // k), requested 32 tiles before they are needed; a tile's entry is then
+  // a lane of a register loaded long before, and is clamped to the pool
+  // where it is used (a bad entry reads the wrong rows, never outside the
+  // pool).
+  auto entries = [&](int base) __attribute__((always_inline)) {
+    const int32_t* table;
+    int pi, row0;
+    page_slot(min(base + lane, n - 1), table, pi, row0);
+    return table[pi];
+  };
+  int pe_cur = 0, pe_next = 0, pe_base = 0;
+  auto issue_paged = [&](auto J, int t) __attribute__((always_inline)) {
+    if (t == pe_base + 64) {
+      pe_cur = pe_next;
+      pe_base += 64;
+    }
+    if (t == pe_base + 32 && pe_base + 64 < n) pe_next = entries(pe_base + 64);
+    const int page =
+        min(max(__builtin_amdgcn_readlane(pe_cur, t - pe_base), 0), a.n_pages - 1);
+    const int32_t* table;
+    int pi, row0;
+    page_slot(t, table, pi, row0);
+    const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>();
+    int lo, nv;
+    tile_span(t, nct, P, k_end, lo, nv);
+    const size_t pbase = (size_t)page * page_bytes + (size_t)kvh * B * D * sizeof(__bf16);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = LPW * wave + i;
+      const int row = RPB * blk + lane / CPR;
+      const int off = (min(row, nv - 1) - row0) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
+      load_kv16(a.remap, (const char*)a.kc + pbase, off, sb + blk * 1024);
+      load_kv16(a.remap, (const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
+    }
+  };
   auto issue = [&](auto J, int t) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      issue_paged(J, t);
+      return;
+    }
     const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>();
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
@@ -149,7 +213,11 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     asm volatile("" ::: "memory");
   };
 
-  // Tiles 0, 1 and 2 are requested before the queries are loaded.
+  // Tiles 0, 1 and 2 are requested before the queries are loaded (paged:
+  // after the first 64 tiles' page entries).
+  if constexpr (PAGED) {
+    if (n > 0) pe_cur = entries(0);
+  }
   if (0 < n) issue(ic<0>{}, 0);
   if (1 < n) issue(ic<1>{}, 1);
   if (2 < n) issue(ic<2>{}, 2);
@@ -419,14 +487,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
 
 }  // namespace
 
-hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {
   const dim3 grid(a.n_units), block(kGqaThreads);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_gqa_kernel<128>), grid, block, 0, s, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((attn_gqa_kernel<64>), grid, block, 0, s, a);
-  else
+  if (head_dim == 128) {
+    if (paged) hipLaunchKernelGGL((attn_gqa_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_gqa_kernel<128, false>), grid, block, 0, s, a);
+  } else if (head_dim == 64) {
+    if (paged) hipLaunchKernelGGL((attn_gqa_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_gqa_kernel<64, false>), grid, block, 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

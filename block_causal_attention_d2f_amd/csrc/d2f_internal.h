@@ -128,7 +128,7 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool paged, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, hipStream_t s);
-hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, bool paged, hipStream_t s);
 // Attention workgroups that fit on one CU at once (0 if unknown).
 int attn_bf16_wgs_per_cu(int head_dim);
 int attn_f32_wgs_per_cu(int head_dim);
