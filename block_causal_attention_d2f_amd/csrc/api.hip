@@ -354,6 +354,10 @@ size_t plan_attention(const d2f_attn_desc_t* d, const int32_t* prefix, const int
   // eight waves 92.8-95.9 us against 97.0-99.2 us for 12 ranges on four
   // waves; with a 131072-token prefix (256-tile ranges) the four-wave plan
   // stays faster (332 vs 350 us), and 512 tokens (3-tile ranges) too.
+  // Contiguous caches only: on the paged loader the same re-plan took 113
+  // vs 99-101 us for the 32K prefix.  Such a paged call therefore cuts its
+  // keys into other ranges than the contiguous call, and the two results
+  // differ by rounding; every other plan is the same for both layouts.
   bool split = false;
   for (const Launch& L : out) split |= L.any_split;
   if (split && !paged) {
