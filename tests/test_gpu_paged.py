@@ -29,6 +29,9 @@ CASES = [
     (6, 32, 4, 128, 32, [2048, 32, 0, 4096, 1024, 96], [3] * 6),
     (10, 28, 4, 64, 16, [16 * i * i for i in range(10)], [4] * 10),
     (16, 64, 8, 128, 8, [8 * i for i in range(16)], [4] * 16),
+    # 142 key tiles in a unit: the page entries of tiles 64.. and 128.. are
+    # fetched while earlier tiles are in flight.
+    (4, 64, 8, 128, 16, [9008, 16, 4096, 8192], [4] * 4),
 ]
 
 
