@@ -196,13 +196,22 @@ def kernel_short_name(name):
     return ident + (f"<{', '.join(args)}>" if args else "")
 
 
+def _counter_files(d):
+    """The counter csv of a rocprofv3 --pmc output directory.  One run per
+    directory: when it holds several (a later run written into the same
+    place), only the newest is read."""
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    return sorted(files, key=os.path.getmtime)[-1:]
+
+
 def _counter_means(d, counter):
     """Average per-dispatch value of `counter` for each kernel in a rocprofv3
     --pmc csv output directory."""
     import csv
     import glob
     sums, counts = {}, {}
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    for f in _counter_files(d):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != counter:
                 continue
@@ -222,7 +231,7 @@ def _dispatch_ns(d, counter, name_part):
     import csv
     import glob
     tot, n = 0.0, 0
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+    for f in _counter_files(d):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
                 tot += float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
