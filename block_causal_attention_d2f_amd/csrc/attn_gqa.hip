@@ -26,17 +26,19 @@
 //  * Keys are processed in halves of 32, software-pipelined within a wave:
 //    while the matrix cores compute the scores of half h + 1, the vector
 //    units turn the scores of half h into probabilities; then half h's PV
-//    product.  The V^T fragments of a half are read from LDS before the
-//    scores of the next half are started, so their latency is covered.
+//    product.  The K fragments of half h + 1 are read from LDS first, then
+//    the V^T fragments of half h: LDS returns reads in order, so the score
+//    MFMAs wait only for theirs, and the V^T reads complete behind them.
 //  * K/V tiles of 64 keys go HBM -> LDS with the direct loads through a
 //    four-stage ring: two tiles stream in while one is computed, one barrier
-//    per tile.
+//    per tile.  Paged caches change only the loader (see issue_paged).
+//  * The reference maximum starts at -FLT_MAX and is raised only when a
+//    half's probability sum exceeds 2^kSlack (see probs).
 //  * Scores are computed transposed (S^T = K Q^T), so a lane holds one query
 //    and the keys of its column, which is the B-operand layout of the PV
 //    product O^T = V^T P^T; V^T is read with ds_read_b64_tr_b16 and the LDS
 //    rows are swizzled as in attn_bf16.hip (conflict-free for both reads).
-//  * Online softmax in base 2 with the lazily raised reference maximum and
-//    per-lane partial sums of attn_bf16.hip.
+//  * Online softmax in base 2 with per-lane partial sums.
 //  * A unit covers all keys of its rows and writes O in bf16 and the LSE
 //    (the planner never cuts these launches' keys into ranges).
 //

@@ -229,8 +229,12 @@ d2f_status_t d2f_attn_combine(const d2f_attn_desc_t* desc, const void* out_a, co
  * table: nothing is copied.  Pages are owned and handed out by the caller.
  *
  * d2f_block_attn_paged computes exactly what d2f_block_attn computes for the
- * same keys (same kernels and work plan; only the K/V addressing differs), with
- * q, out, lse laid out as there.  Requirements: bf16, head_dim 64 or 128,
+ * same keys, with q, out, lse laid out as there.  It uses the same kernels and
+ * work plan, so the results are bit-identical, with one exception: a call
+ * whose keys are cut into few long ranges (a long prefix over few heads),
+ * which d2f_block_attn re-plans for one eight-wave workgroup per CU, keeps the
+ * four-wave plan here; its ranges then differ, and so do the results, by
+ * rounding.  Requirements: bf16, head_dim 64 or 128,
  * block_size a power of two >= 8 (D2F_ERR_UNSUPPORTED otherwise); every
  * prefix_len_host[b] a multiple of block_size (D2F_ERR_INVALID_ARG; the
  * cache holds whole blocks) with P/B <= table_stride (D2F_ERR_CAPACITY);
