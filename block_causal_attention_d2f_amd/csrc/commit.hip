@@ -383,8 +383,12 @@ __global__ __launch_bounds__(kCommitThreads) void vocab_reduce_kernel(const Comm
   if (AUX == kAuxSecond && a.early_gap != nullptr && threadIdx.x == 0 &&
       (int)blockIdx.x < a.n_groups)
     a.ws_gmin[blockIdx.x] = 0x7f800000u;
-  const int row = blockIdx.x / a.n_chunks;
-  const int ck = blockIdx.x - row * a.n_chunks;
+  // Workgroups are renumbered so that each XCD streams a contiguous run of
+  // rows (measured on MI355X: Dream-shaped block 64, 934 MB, 138.9 vs
+  // 144.6 us per pass; the smaller passes unchanged).
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int row = u / a.n_chunks;
+  const int ck = u - row * a.n_chunks;
   if (a.mask_state[row] != D2F_MASKED) return;
   float4 part;
   reduce_chunk<VEC, AUX>(a, row, ck, part);
