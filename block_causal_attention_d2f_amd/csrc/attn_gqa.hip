@@ -54,11 +54,16 @@
 // split each tile's keys and join through LDS at the end, which halves the
 // LDS reads per tile (no gain at 48 to 128 rows per unit).  Cutting the keys
 // into ranges merged by attn_merge.hip lost to the merge pass at every
-// size tried.  What bounds it: per 64-key tile and SIMD, the
-// matrix work (3 blocks x 512 cycles), the softmax's vector work (v_exp_f32
-// runs at a quarter of the VALU rate; ~480 cycles per block) and the LDS
-// reads (K fragments go through ds_read_b128 at ~130 B/clock per CU, V^T
-// through ds_read_b64_tr_b16 at ~250) are of the same size.
+// size tried, and so did wave groups a phase apart (waves 0-3 and 4-7
+// placing the tile's barrier on either side of a softmax phase: 54 vs 50 us
+// for two window blocks of 32).  What bounds it: per 64-key tile and SIMD,
+// the matrix work (3 blocks x 512 cycles), the softmax's vector work
+// (v_exp_f32 runs at a quarter of the VALU rate) and the LDS reads (K
+// fragments through ds_read_b128 at ~237 B/clock per CU, V^T through
+// ds_read_b64_tr_b16 at ~218) are of the same size.  A probe that issues the
+// same instruction mix with no dependencies reaches about 1.25 PFLOP/s for
+// this block layout, against 0.7 here: the rest is how the waves' matrix
+// and vector phases overlap.
 
 #include "attn_lds.h"
 
