@@ -71,7 +71,8 @@ enum { D2F_CONSERVATIVE = 0, D2F_AGGRESSIVE = 1 };
  *  batch           requests in the call (>= 0)
  *  n_heads_q       query heads; n_heads_kv KV heads; n_heads_q % n_heads_kv == 0
  *                  and query head h reads KV head h / (n_heads_q / n_heads_kv)
- *  head_dim        D: 128 for bf16 (the MFMA path); 32, 64 or 128 for f32
+ *  head_dim        D: 64 or 128 for bf16 (the MFMA path); 32, 64 or 128 for
+ *                  f32; other values return D2F_ERR_UNSUPPORTED
  *  block_size      B >= 1, tokens per D2F block
  *  max_win_blocks  window capacity in blocks; Wmax = max_win_blocks * B
  *  cache_capacity  token slots per (request, KV head) in the cache arrays
