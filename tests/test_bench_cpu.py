@@ -91,3 +91,20 @@ def test_kernel_short_name_reads_mangled_and_demangled_names():
         "_ZN3d2f12_GLOBAL__N_119vocab_reduce_kernelILb1ELi0EEEvNS_10CommitArgsE") == \
         "vocab_reduce_kernel<true, 0>"
     assert bench.kernel_short_name("void at::native::fill_kernel(int)") is None
+
+
+def test_stall_breakdown_shares_and_per_wave_counts():
+    """Shares are the wave-cycle counters over SQ_WAVE_CYCLES, counts are per
+    wave, and the co-execution share is taken of the MFMA busy cycles."""
+    v = {c: 0.0 for cs in bench.STALL_COUNTERS for c in cs}
+    v.update({"SQ_WAVE_CYCLES": 1000.0, "SQ_ACTIVE_INST_ANY": 300.0, "SQ_WAIT_ANY": 400.0,
+              "SQ_WAIT_INST_ANY": 250.0, "SQ_ACTIVE_INST_VALU": 200.0, "SQ_ACTIVE_INST_SCA": 50.0,
+              "SQ_WAVES": 10.0, "SQ_INSTS_MFMA": 70.0, "SQ_INSTS_SALU": 35.0,
+              "SQ_VALU_MFMA_BUSY_CYCLES": 2048.0, "SQ_VALU_MFMA_COEXEC_CYCLES": 512.0})
+    r = bench.stall_breakdown(v)
+    s = r["share_of_wave_cycles"]
+    assert s["issuing_any"] == 0.3 and s["waiting_on_counters_or_barrier"] == 0.4
+    assert s["waiting_to_issue"] == 0.25 and s["valu"] == 0.2 and s["scalar"] == 0.05
+    assert r["instructions_per_wave"]["mfma"] == 7.0 and r["instructions_per_wave"]["salu"] == 3.5
+    assert r["mfma_busy_cycles_per_simd"] == 2 and r["coexec_share_of_mfma_busy"] == 0.25
+    assert all(len(cs) <= 8 for cs in bench.STALL_COUNTERS)  # one pass holds <= 8 SQ counters
