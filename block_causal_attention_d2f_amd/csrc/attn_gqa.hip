@@ -43,9 +43,12 @@
 //    (the planner never cuts these launches' keys into ranges).
 //
 // Measured on MI355X (8 requests, 28 query / 4 KV heads, 2048 cached keys,
-// three window blocks of 64: 1344 query rows per KV head): 66-70 us against
+// three window blocks of 64: 1344 query rows per KV head): 64-68 us against
 // 76 us for the first version of this kernel and 81-85 us for attn_bf16.hip
-// on the same machines.  Tried and not faster: scheduling-group barriers
+// on the same machines; 2-4% of that came from testing a half for masking
+// against two precomputed half indices (h_cmask, h_wmask) instead of
+// recomputing its tile's span, and 3-6% from the load policy being a
+// template argument.  Tried and not faster: scheduling-group barriers
 // that interleave one MFMA with four vector instructions (81 us), a raised
 // wave priority while the scores' MFMAs issue (76 us), LDS addresses
 // recomputed in every step to save registers (73 us), a ring of three or
@@ -111,6 +114,11 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   const int k_full = a.cache_only ? P : P + min(W, ((r0 / G) / B + 1) * B);  // every row sees
   const int nct = cache_tiles(P);
   const int n = nct + window_tiles(P, k_end);  // tiles of the unit (all its keys)
+  // Halves that need a mask: those of a partial last cache tile from the
+  // first one that ends past P, and the window halves from the first one
+  // that ends past k_full (the key end every row of the unit reaches).
+  const int h_cmask = (P & 63) ? 2 * (nct - 1) + ((P & 63) >= 32 ? 1 : 0) : 2 * nct;
+  const int h_wmask = 2 * nct + (k_full - P) / 32;
 
   const size_t head_c = (((size_t)rb * a.hkv + kvh) * (size_t)a.cap + a.req[ri].key_off) * D;
   const size_t head_w = ((size_t)rb * a.hkv + kvh) * (size_t)a.wmax * D;
@@ -309,10 +317,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   auto prepare = [&](auto QBc, int h, f32x4 (&s)[2][2]) __attribute__((always_inline)) {
     constexpr int QB = decltype(QBc)::value;
     if constexpr (QB > 0) {
-      int lo, nv;
-      tile_span(h >> 1, nct, P, k_end, lo, nv);
-      const int klo = lo + 32 * (h & 1), nvh = nv - 32 * (h & 1);
-      if (nvh < 32 || klo + 32 > k_full) {
+      if ((h >= h_cmask && h < 2 * nct) || h >= h_wmask) {
+        int lo, nv;
+        tile_span(h >> 1, nct, P, k_end, lo, nv);
+        const int klo = lo + 32 * (h & 1), nvh = nv - 32 * (h & 1);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int lim = min(nvh, my_lim[qb] - klo);
