@@ -17,12 +17,22 @@
 // planner), so the same stream feeds up to 4x the MFMA work.
 //
 // Design (one workgroup = 8 waves = one work unit, one workgroup per CU):
-//  * The unit's 16-row query blocks are dealt to the waves round-robin
-//    (block b -> wave b mod 8), so a wave owns one or two blocks and the two
-//    waves that share a SIMD (w and w + 4) never hold more blocks between
-//    them than any other pair plus one.  Every wave runs over every key of
-//    the unit: it owns its rows' online-softmax state outright, and no join
-//    is needed.
+//  * Units of more than 8 blocks: the unit's 16-row query blocks are dealt
+//    to the waves round-robin (block b -> wave b mod 8), so a wave owns one
+//    or two blocks and the two waves that share a SIMD (w and w + 4) never
+//    hold more blocks between them than any other pair plus one.  Every wave
+//    runs over every key of the unit: it owns its rows' online-softmax state
+//    outright, and no join is needed.
+//  * Units of at most 8 blocks (KS): waves 0-3 take keys 0-31 of every tile
+//    and waves 4-7 keys 32-63.  Each group holds all of the unit's blocks,
+//    dealt round-robin over its four waves, and the second group's deal is
+//    rotated by two waves, so a SIMD's pair of waves holds one block and its
+//    neighbour's two rather than two and two: a 6-block unit puts three
+//    half-tile blocks on every SIMD instead of four on two of them and two
+//    on the others.  Each wave keeps the online-softmax state of its keys;
+//    at the end the second group hands (m, l, O) to the first through LDS
+//    and the first joins the two exactly.  Measured on MI355X (Dream-7B
+//    shape, block 32, 96-row units): 43.2-44.7 vs 47.0-48.1 us.
 //  * Keys are processed in halves of 32, software-pipelined within a wave:
 //    while the matrix cores compute the scores of half h + 1, the vector
 //    units turn the scores of half h into probabilities; then half h's PV
@@ -74,6 +84,7 @@ namespace d2f {
 namespace {
 
 constexpr int kGqaWaves = kGqaThreads / 64;
+constexpr int kGqaKsMaxRows = 128;  // units up to 8 blocks split each tile's keys
 constexpr int kGqaStages = 4;
 constexpr float kSlackSum = 256.f;  // 2^kSlack: largest per-lane probability sum kept
 
@@ -83,8 +94,9 @@ constexpr int wait_vm_lgkm0(int v) { return (v & 15) | (((v >> 4) & 3) << 14) | 
 // PAGED: K/V rows are found through the page tables (AttnArgs), in pages of
 // a power of two >= 8 rows.  SHARED (a.remap): several units read each KV
 // head's tiles, so units are numbered XCD-contiguously and the tile loads keep
-// the default cache policy; otherwise they are non-temporal.
-template <int D, bool PAGED, bool SHARED>
+// the default cache policy; otherwise they are non-temporal.  KS: the unit
+// has at most 8 blocks and its two wave groups split each tile's keys.
+template <int D, bool PAGED, bool SHARED, bool KS>
 __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs a) {
   constexpr int RS = D * 2;              // LDS row bytes
   constexpr int KSTEPS = D / 32;         // MFMA k-steps over head_dim
@@ -131,7 +143,14 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lc = lane & 15, lg = lane >> 4;
   const int nblk = (min(R, rows - r0) + 15) >> 4;  // 16-row blocks with a valid row
-  const int nq = (wave < nblk) + (wave + kGqaWaves < nblk);  // this wave's blocks: 0, 1, 2
+  // KS (units of at most 8 blocks): waves 0-3 take keys 0-31 of every tile,
+  // waves 4-7 keys 32-63.  Waves 0-3 hold blocks w, w + 4; wave 4 + w holds
+  // the blocks of wave (w + 2) mod 4, so the two waves of a SIMD (w and
+  // w + 4) hold at most three blocks between them when a unit has six.
+  const int kg = KS ? (wave >> 2) : 0;                  // key half of this wave
+  const int wb = KS ? (((wave & 3) + 2 * kg) & 3) : wave;  // its first block
+  constexpr int BSTRIDE = KS ? 4 : kGqaWaves;
+  const int nq = (wb < nblk) + (wb + BSTRIDE < nblk);  // this wave's blocks: 0, 1, 2
 
   // Loader: wave w copies 1 KB blocks w, w + 8, ... of each of K and V; lane
   // l of block j carries the 16 bytes that belong at LDS position (row
@@ -246,7 +265,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   bf16x8 qf[2][KSTEPS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = r0 + 16 * (wave + kGqaWaves * qb) + lc;
+    const int row = r0 + 16 * (wb + BSTRIDE * qb) + lc;
     row_ok[qb] = qb < nq && row < r0 + R && row < rows;
     my_i[qb] = row_ok[qb] ? row / G : 0;
     my_h[qb] = kvh * G + (row_ok[qb] ? row % G : 0);
@@ -471,10 +490,97 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       if (t + 3 < n) tile(ic<3>{}, t + 3);
     }
   };
+  // KS: one half per tile.  Step t reads K of tile t + 1 (landed at barrier
+  // t) and V of tile t; after barrier t every wave is past step t - 1, the
+  // last to read tile t - 1, whose stage then receives tile t + 3.
+  auto run_ks = [&](auto QBc) __attribute__((always_inline)) {
+    {
+      bf16x8 ka[2][KSTEPS];
+      kread(ic<0>{}, QBc, kg, ka);
+      smma(QBc, ka, sa);
+    }
+    prepare(QBc, kg, sa);
+    auto tile = [&](auto J, int t) __attribute__((always_inline)) {
+      constexpr int JK = decltype(J)::value;
+      f32x4 (&scur)[2][2] = (JK & 1) ? sb : sa;
+      f32x4 (&snext)[2][2] = (JK & 1) ? sa : sb;
+      barrier(t + 2 < n ? 1 : 0);
+      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
+      bf16x8 va[DBLK];
+      if (t + 1 < n) {
+        bf16x8 ka[2][KSTEPS];
+        kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2 + kg, ka);
+        vload(J, QBc, 2 * t + kg, va);
+        smma(QBc, ka, snext);
+      } else {
+        vload(J, QBc, 2 * t + kg, va);
+      }
+      probs(QBc, scur);
+      pv(QBc, va);
+      if (t + 1 < n) prepare(QBc, 2 * t + 2 + kg, snext);
+    };
+    for (int t = 0; t < n; t += NST) {
+      tile(ic<0>{}, t);
+      if (t + 1 < n) tile(ic<1>{}, t + 1);
+      if (t + 2 < n) tile(ic<2>{}, t + 2);
+      if (t + 3 < n) tile(ic<3>{}, t + 3);
+    }
+  };
   if (n > 0) {
-    if (nq == 2) run(ic<2>{});
-    else if (nq == 1) run(ic<1>{});
-    else run(ic<0>{});
+    if constexpr (KS) {
+      if (nq == 2) run_ks(ic<2>{});
+      else if (nq == 1) run_ks(ic<1>{});
+      else run_ks(ic<0>{});
+    } else {
+      if (nq == 2) run(ic<2>{});
+      else if (nq == 1) run(ic<1>{});
+      else run(ic<0>{});
+    }
+  }
+
+  // KS: waves 4-7 hand (m, l, O) of each block to the wave of keys 0-31
+  // through LDS (same lane, same register layout); it joins the two exactly.
+  if constexpr (KS) {
+    constexpr int OB = DBLK * 4 * 64;  // floats of one block's O
+    static_assert(4 * OB * 4 <= SB, "four blocks' O fit one stage");
+    __builtin_amdgcn_s_waitcnt(kVmLgkmZero);
+    __builtin_amdgcn_s_barrier();  // every wave is past its last read of the stages
+    auto oslot = [&](int b) {
+      return (b < 4 ? (float*)stage_buf<0, SB>() : (float*)stage_buf<1, SB>()) + (b & 3) * OB;
+    };
+    float* mlslot = (float*)stage_buf<2, SB>();
+    if (kg == 1) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (qb >= nq) continue;
+        const int b = wb + 4 * qb;
+        float* xo = oslot(b);
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) *(f32x4*)(xo + (d * 64 + lane) * 4) = o[d][qb];
+        mlslot[(b * 64 + lane) * 2 + 0] = m_run[qb];
+        mlslot[(b * 64 + lane) * 2 + 1] = l_run[qb];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVmLgkmZero);
+    __builtin_amdgcn_s_barrier();
+    if (kg == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        if (qb >= nq) continue;
+        const int b = wb + 4 * qb;
+        const float* xo = oslot(b);
+        const float m1 = mlslot[(b * 64 + lane) * 2 + 0];
+        const float l1 = mlslot[(b * 64 + lane) * 2 + 1];
+        const float m = fmaxf(m_run[qb], m1);
+        const float w0 = __builtin_amdgcn_exp2f(m_run[qb] - m);
+        const float w1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+          o[d][qb] = o[d][qb] * w0 + *(const f32x4*)(xo + (d * 64 + lane) * 4) * w1;
+        l_run[qb] = l_run[qb] * w0 + l1 * w1;
+        m_run[qb] = m;
+      }
+    }
   }
 
   // Per-lane partial sums to per-query sums (the 4 lanes of a query column),
@@ -486,7 +592,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (!row_ok[qb]) continue;
+    if (!row_ok[qb] || kg != 0) continue;
     const float inv = 1.0f / l_run[qb];
     __bf16* op = (__bf16*)a.out + (((size_t)rb * a.hq + my_h[qb]) * a.wmax + my_i[qb]) * D;
 #pragma unroll
@@ -504,10 +610,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
 
 }  // namespace
 
+template <int D, bool PAGED, bool KS>
+void launch_gqa_ks(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.remap) hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, true, KS>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, false, KS>), grid, block, 0, s, a);
+}
+// Units of at most kGqaKsMaxRows rows split each tile's keys between the two
+// wave groups (KS); larger units give every wave all the keys of its blocks.
 template <int D, bool PAGED>
 void launch_gqa_policy(const AttnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.remap) hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_gqa_kernel<D, PAGED, false>), grid, block, 0, s, a);
+  if (a.qrows <= kGqaKsMaxRows) launch_gqa_ks<D, PAGED, true>(a, grid, block, s);
+  else launch_gqa_ks<D, PAGED, false>(a, grid, block, s);
 }
 
 hipError_t launch_attn_gqa(const AttnArgs& a, int head_dim, bool paged, hipStream_t s) {

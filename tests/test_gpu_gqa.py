@@ -87,11 +87,13 @@ def test_gqa_edge_shapes(case):
     compare_attn(sh, out, lse, ref_o, ref_l, pairs=pairs, label=f"gqa-edge-G{hq // hkv}-B{b}")
 
 
-def test_gqa_deterministic_and_causal():
+@pytest.mark.parametrize("nwin", [[4, 4, 3, 2, 4, 4], [2, 2, 1, 1, 2, 2]])
+def test_gqa_deterministic_and_causal(nwin):
     """Two runs bit-identical; re-drawing the last window block (its q, K and
-    V) leaves the rows of the earlier blocks bit-identical."""
-    sh = W.make_shape(6, 32, 4, 128, 64, [2048, 65, 0, 1000, 1, 64], [4, 4, 3, 2, 4, 4],
-                      dtype="bf16")
+    V) leaves the rows of the earlier blocks bit-identical.  The second draw
+    has 80-row units (80 rows per CU): each tile's keys are split between
+    the two wave groups and joined at the end."""
+    sh = W.make_shape(6, 32, 4, 128, 64, [2048, 65, 0, 1000, 1, 64], nwin, dtype="bf16")
     assert _rows(sh) >= MIN_ROWS
     x = poisoned_inputs(sh, seed=5)
     o1, l1 = run_attn(sh, x, out_fill=7.0)
@@ -114,17 +116,19 @@ def test_gqa_deterministic_and_causal():
     compare_attn(sh, o3, l3, ref_o, ref_l, pairs=pairs, label="gqa-redrawn")
 
 
-def test_gqa_key_range():
+@pytest.mark.parametrize("bsz,nb", [(64, 6), (32, 8)])
+def test_gqa_key_range(bsz, nb):
     """The window's queries over a cache key range (the outside-block part)
-    on a grouped-query shape: against the oracle's range attention."""
+    on a grouped-query shape: against the oracle's range attention (block 32:
+    96-row units, keys split between the wave groups)."""
     import block_causal_attention_d2f_amd as d2f
     from oracle import attention as OA
-    sh = W.make_shape(6, 28, 4, 128, 64, [2048, 1500, 700, 64, 3000, 129], [4] * 6,
-                      dtype="bf16")
+    prefix = [2048, 1500, 700, 64, 3000, 129, 2100, 999][:nb]
+    sh = W.make_shape(nb, 28, 4, 128, bsz, prefix, [4 if bsz == 64 else 3] * nb, dtype="bf16")
     assert _rows(sh) >= MIN_ROWS
     x = poisoned_inputs(sh, seed=6)
-    lo = [100, 0, 63, 1, 2500, 0]
-    hi = [2048, 1437, 700, 64, 3000, 129]
+    lo = [100, 0, 63, 1, 2500, 0, 2099, 500][:nb]
+    hi = [2048, 1437, 700, 64, 3000, 129, 2100, 999][:nb]
     out = torch.full_like(x["q"], 7.0)
     lse = torch.full(x["q"].shape[:3], 7.0, device="cuda")
     d2f.d2f_block_attn_range(x["q"], x["k_cache"], x["v_cache"], lo, hi, sh.n_win_blocks,
