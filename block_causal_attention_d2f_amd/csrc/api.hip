@@ -274,9 +274,11 @@ bool use_gqa(const d2f_attn_desc_t* d, const int32_t* nwin, long long cus) {
 // KV head) over all of its keys -- R a multiple of 16, at most kGqaMaxRows
 // -- one workgroup of eight waves, one workgroup per CU.  R is the launch's
 // query rows per CU, so that each CU gets about one unit and every K/V tile
-// it streams feeds as many rows as the launch allows.  Keys are never split
-// (the calls this kernel takes have at least kGqaMinRowsPerCU rows per CU,
-// so the units cover the CUs), and no workspace is needed.
+// it streams feeds as many rows as the launch allows.  Keys are never cut
+// into ranges across units (the calls this kernel takes have at least
+// kGqaMinRowsPerCU rows per CU, so the units cover the CUs; within a unit of
+// at most 8 blocks the kernel's two wave groups split each tile's keys and
+// join in LDS), and no workspace is needed.
 size_t plan_gqa(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t* nwin,
                 std::vector<Launch>& out, const int32_t* key_off, long long cus) {
   const bool cache_only = key_off != nullptr;
