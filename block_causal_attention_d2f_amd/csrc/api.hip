@@ -256,10 +256,11 @@ size_t plan_pass(const d2f_attn_desc_t* d, const int32_t* prefix, const int32_t*
 // Measured on MI355X with 28 query / 4 KV heads, 8 requests and 2048 cached
 // keys: 1344 rows per KV head (168 per CU) 64-68 us against 81-85 us on the
 // four-wave kernels; 672 rows (84 per CU, 96-row units, keys split between
-// the wave groups) 43-46 vs 51.6 us; 336 rows (42 per CU) 37.5 us with
-// 48-row units against 34.3 us on the eight-wave kernel (32.5-33.3 vs
-// 33.1-33.6 us with the key split), so those stay there.
-constexpr long long kGqaMinRowsPerCU = 64;
+// the wave groups) 43-46 vs 51.6 us; 336 rows (42 per CU, 48-row units, keys
+// split) 33.7 vs 35.0 us on the eight-wave kernel, and on a paged cache 40.5
+// vs 45.6 us.  (Before the key split, 48-row units took 37.5 us, and such
+// calls stayed on the eight-wave kernel.)
+constexpr long long kGqaMinRowsPerCU = 40;
 constexpr int kGqaMinGroup = 2;  // query heads per KV head
 bool use_gqa(const d2f_attn_desc_t* d, const int32_t* nwin, long long cus) {
   if (d->dtype != D2F_BF16 || (d->head_dim != 64 && d->head_dim != 128) ||

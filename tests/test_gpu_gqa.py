@@ -2,8 +2,10 @@
 fp64 oracle, through the C ABI.
 
 The library sends a bf16 call there when the query heads share KV heads and
-the call has at least 64 query rows per compute unit (16384 rows on the
-256-CU MI355X); every shape below is above that.  The draws vary batch, KV
+the call has at least 40 query rows per compute unit (10240 rows on the
+256-CU MI355X).  The random draws keep at least 64 rows per compute unit;
+the edge cases go down to 42 (48-row units, keys split between the wave
+groups).  The draws vary batch, KV
 heads, group size, head_dim, block size and window, with prefixes that mix
 tile-boundary lengths (0, 1, 63, 64, 65) and uniform ones; unread cache
 slots and window rows are NaN and padding rows must stay untouched."""
@@ -16,7 +18,8 @@ from parity import compare_attn, oracle_attn, poisoned_inputs, run_attn, say
 
 pytestmark = pytest.mark.gpu
 
-MIN_ROWS = 64 * 256  # query rows that route a grouped-query bf16 call to the kernel
+MIN_ROWS = 64 * 256  # lower bound of the random draws' query rows
+ROUTE_ROWS = 40 * 256  # query rows that route a grouped-query bf16 call to the kernel
 
 
 def _rows(sh):
@@ -74,11 +77,13 @@ def test_random_gqa_shapes(k):
     (16, 64, 8, 128, 8, [7 * i * i for i in range(16)], [4] * 16),      # B = 8: 4 blocks per tile
     (2, 128, 8, 128, 48, [0, 777], [3, 3]),                              # group 16, B = 48
     (8, 28, 4, 128, 32, [2048, 2047, 1, 64, 65, 0, 1500, 2048], [3] * 8), # Dream shape, B = 32
+    (8, 28, 4, 128, 16, [2048, 2047, 1, 64, 65, 0, 1500, 2048], [3] * 8), # B = 16: 48-row units
+    (8, 28, 4, 64, 16, [16, 0, 700, 2048, 33, 64, 1, 999], [3] * 8),      # the same, head_dim 64
 ])
 def test_gqa_edge_shapes(case):
     nb, hq, hkv, d, b, prefix, nwin = case
     sh = W.make_shape(nb, hq, hkv, d, b, prefix, nwin, dtype="bf16", extra_capacity=5)
-    assert _rows(sh) >= MIN_ROWS
+    assert _rows(sh) >= ROUTE_ROWS
     say(f"--- gqa edge {case}: rows {_rows(sh)}")
     x = poisoned_inputs(sh, seed=nb + hq)
     out, lse = run_attn(sh, x, out_fill=7.0)

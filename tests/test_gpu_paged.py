@@ -22,10 +22,12 @@ CASES = [
     (1, 8, 8, 128, 32, [4096], [3]),            # B = 32, a long prefix split across units
     (2, 28, 4, 128, 64, [2048, 1024], [3, 2]),  # Dream-like GQA 7, B = 64
     (3, 4, 2, 128, 16, [48, 96, 32], [2, 0, 1]),  # an idle request
-    # Grouped-query shapes with >= 64 query rows per CU (the grouped-query
-    # kernel's paged loader): Dream-like B = 64, B = 32 with ragged prefixes,
+    # Grouped-query shapes with >= 40 query rows per CU (the grouped-query
+    # kernel's paged loader): Dream-like B = 64, B = 16 (48-row units with
+    # keys split between the wave groups), B = 32 with ragged prefixes,
     # head_dim 64 with 16-row pages, 8-row pages.
     (8, 28, 4, 128, 64, [2048, 1984, 64, 0, 1024, 2048, 512, 1920], [3] * 8),
+    (8, 28, 4, 128, 16, [2048, 1984, 64, 0, 1024, 2048, 512, 1920], [3] * 8),
     (6, 32, 4, 128, 32, [2048, 32, 0, 4096, 1024, 96], [3] * 6),
     (10, 28, 4, 64, 16, [16 * i * i for i in range(10)], [4] * 10),
     (16, 64, 8, 128, 8, [8 * i for i in range(16)], [4] * 16),
