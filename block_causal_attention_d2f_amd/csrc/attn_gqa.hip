@@ -32,7 +32,9 @@
 //    on the others.  Each wave keeps the online-softmax state of its keys;
 //    at the end the second group hands (m, l, O) to the first through LDS
 //    and the first joins the two exactly.  Measured on MI355X (Dream-7B
-//    shape, block 32, 96-row units): 43.2-44.7 vs 47.0-48.1 us.
+//    shape, block 32, 96-row units): 43.2-44.7 vs 47.0-48.1 us.  Each step
+//    of this mode reads the next tile's V^T fragments at its end, before
+//    the barrier.
 //  * Keys are processed in halves of 32, software-pipelined within a wave:
 //    while the matrix cores compute the scores of half h + 1, the vector
 //    units turn the scores of half h into probabilities; then half h's PV
@@ -501,12 +503,18 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     }
   };
   // KS: one half per tile.  Step t reads K of tile t + 1 (landed at barrier
-  // t) and V of tile t; after barrier t every wave is past step t - 1, the
-  // last to read tile t - 1, whose stage then receives tile t + 3.
+  // t) after the barrier, and at its end, before barrier t + 1, the V^T
+  // fragments of tile t + 1 that step t + 1 multiplies, so only the K reads
+  // queue at the LDS behind the barrier (measured on MI355X, Dream-shaped
+  // calls: block 16 31.1-31.3 vs 31.4-31.5 us, block 32 39.7-39.9 vs
+  // 40.8-40.9 us).  Tile t - 1 is last read in step t - 2, so after barrier
+  // t its stage receives tile t + 3.
   auto run_ks = [&](auto QBc) __attribute__((always_inline)) {
+    bf16x8 va[DBLK];
     {
       bf16x8 ka[2][KSTEPS];
       kread(ic<0>{}, QBc, kg, ka);
+      vload(ic<0>{}, QBc, kg, va);
       smma(QBc, ka, sa);
     }
     prepare(QBc, kg, sa);
@@ -516,18 +524,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       f32x4 (&snext)[2][2] = (JK & 1) ? sa : sb;
       barrier(t + 2 < n ? 1 : 0);
       if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
-      bf16x8 va[DBLK];
       if (t + 1 < n) {
         bf16x8 ka[2][KSTEPS];
         kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2 + kg, ka);
-        vload(J, QBc, 2 * t + kg, va);
         smma(QBc, ka, snext);
-      } else {
-        vload(J, QBc, 2 * t + kg, va);
       }
       probs(QBc, scur);
       pv(QBc, va);
-      if (t + 1 < n) prepare(QBc, 2 * t + 2 + kg, snext);
+      if (t + 1 < n) {
+        vload(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2 + kg, va);
+        prepare(QBc, 2 * t + 2 + kg, snext);
+      }
     };
     for (int t = 0; t < n; t += NST) {
       tile(ic<0>{}, t);
