@@ -87,6 +87,8 @@ def block_attn(q, k_cache, v_cache, k_win, v_win, prefix_len, n_win_blocks, bloc
         g = h // group
         P = int(prefix_len[b])
         W = int(n_win_blocks[b]) * int(block_size)
+        if W == 0:
+            continue  # an idle request has no window rows, hence no outputs
         key = (b, g)
         if key not in cache_f64:
             kk = np.concatenate([as_f64(k_cache[b, g, :P]), as_f64(k_win[b, g, :W])], axis=0)

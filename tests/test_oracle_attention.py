@@ -252,3 +252,23 @@ def test_rows_past_window_are_nan_and_pairs_subset():
     o2, _ = _run(sh, x, pairs=[(1, 1)])
     np.testing.assert_array_equal(o2[1, 1], out[1, 1])
     assert np.isnan(o2[0]).all() and np.isnan(o2[1, 0]).all()
+
+
+def test_idle_requests_have_no_rows_and_leave_the_others_alone():
+    # Requests 1 (no cache, no window) and 2 (cache only) are idle: they have
+    # no window rows, so no outputs; each active request's rows equal those of
+    # the same request attended on its own.
+    prefix, nwin, B = [5, 0, 7, 3], [2, 0, 0, 1], 2
+    sh = W.make_shape(4, 4, 2, 8, B, prefix, nwin, dtype="f32", max_win_blocks=2)
+    x = _inputs64(sh, seed=11)
+    out, lse = _run(sh, x)
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert np.isnan(lse[1]).all() and np.isnan(lse[2]).all()
+    for b in (0, 3):
+        one = W.make_shape(1, 4, 2, 8, B, [prefix[b]], [nwin[b]], dtype="f32", max_win_blocks=2,
+                           cache_capacity=sh.cache_capacity)
+        y = {k: v[b:b + 1] for k, v in x.items()}
+        o1, l1 = _run(one, y)
+        rows = nwin[b] * B
+        np.testing.assert_array_equal(out[b, :, :rows], o1[0, :, :rows])
+        np.testing.assert_array_equal(lse[b, :, :rows], l1[0, :, :rows])
