@@ -5,7 +5,8 @@ The library sends a bf16 call there when the query heads share KV heads and
 the call has at least 40 query rows per compute unit (10240 rows on the
 256-CU MI355X).  The random draws keep at least 64 rows per compute unit;
 the edge cases go down to 42 (48-row units, keys split between the wave
-groups).  The draws vary batch, KV
+groups), and a second set of draws spans 30-64 rows per compute unit, on both
+sides of the routing threshold, with the paged layout checked bit for bit.  The draws vary batch, KV
 heads, group size, head_dim, block size and window, with prefixes that mix
 tile-boundary lengths (0, 1, 63, 64, 65) and uniform ones; unread cache
 slots and window rows are NaN and padding rows must stay untouched."""
@@ -14,7 +15,7 @@ import pytest
 import torch
 
 import workloads as W
-from parity import compare_attn, oracle_attn, poisoned_inputs, run_attn, say
+from parity import compare_attn, oracle_attn, poisoned_inputs, run_attn, say, to_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +69,55 @@ def test_random_gqa_shapes(k):
     for b in range(sh.batch):
         assert (o[b, :, sh.win_rows(b):] == 7.0).all()
         assert (lo[b, :, sh.win_rows(b):] == 7.0).all()
+
+
+def _draw_near_threshold(k):
+    """Whole-block prefixes (so the paged layout applies), 30-64 query rows per
+    compute unit: both sides of the grouped-query routing threshold, and the
+    units of at most 8 blocks whose wave groups split each tile's keys."""
+    rng = np.random.default_rng(12000 + k)
+    while True:
+        nb = int(rng.integers(2, 13))
+        hkv = int(rng.choice([2, 4, 8]))
+        g = int(rng.choice([2, 4, 7, 8]))
+        d = int(rng.choice([64, 128]))
+        bsz = int(rng.choice([8, 16, 32]))
+        mw = int(rng.integers(1, 5))
+        nwin = [int(rng.integers(0, mw + 1)) for _ in range(nb)]
+        nwin[0] = mw
+        prefix = [int(rng.integers(0, 2600)) // bsz * bsz for _ in range(nb)]
+        sh = W.make_shape(nb, hkv * g, hkv, d, bsz, prefix, nwin, dtype="bf16",
+                          max_win_blocks=mw, extra_capacity=int(rng.integers(0, 9)))
+        if 30 * 256 <= _rows(sh) < MIN_ROWS:
+            return sh
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_random_gqa_near_threshold(k):
+    import block_causal_attention_d2f_amd as d2f
+    sh = _draw_near_threshold(k)
+    say(f"--- gqa near-threshold draw {k}: {sh} rows {_rows(sh)}")
+    x = poisoned_inputs(sh, seed=500 + k)
+    out, lse = run_attn(sh, x, out_fill=7.0)
+    rng = np.random.default_rng(600 + k)
+    active = [b for b in range(sh.batch) if sh.win_rows(b) > 0]
+    pairs = sorted({(int(rng.choice(active)), int(rng.integers(0, sh.n_heads_q)))
+                    for _ in range(8)})
+    ref_o, ref_l = oracle_attn(sh, x, pairs=pairs)
+    compare_attn(sh, out, lse, ref_o, ref_l, pairs=pairs, label=f"gqa-near{k}")
+    o = out.float().cpu().numpy()
+    lo = lse.cpu().numpy()
+    for b in range(sh.batch):
+        assert (o[b, :, sh.win_rows(b):] == 7.0).all()
+        assert (lo[b, :, sh.win_rows(b):] == 7.0).all()
+    kp, vp, pt, wp = to_pages(sh, x, seed=k)
+    o2 = torch.full_like(x["q"], 7.0)
+    l2 = torch.full(x["q"].shape[:3], 7.0, device="cuda")
+    d2f.d2f_block_attn_paged(x["q"], kp, vp, pt, wp, sh.prefix_len, sh.n_win_blocks,
+                             out=o2, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), "paged outputs differ"
+    assert torch.equal(l2, lse), "paged lse differs"
 
 
 @pytest.mark.parametrize("case", [
