@@ -71,7 +71,11 @@
 // into ranges merged by attn_merge.hip lost to the merge pass at every
 // size tried, and so did wave groups a phase apart (waves 0-3 and 4-7
 // placing the tile's barrier on either side of a softmax phase: 54 vs 50 us
-// for two window blocks of 32).  What bounds it: per 64-key tile and SIMD,
+// for two window blocks of 32).  Also slower in the key-split mode: every
+// LDS read issued a step ahead into a second register set (block 16: 33.1 vs
+// 31.5 us), a barrier every second step (33.5 vs 31.1 us), and waves 4-7
+// forming their probabilities before their score MFMAs (32.7 vs 31.1 us).
+// What bounds it: per 64-key tile and SIMD,
 // the matrix work (3 blocks x 512 cycles), the softmax's vector work
 // (v_exp_f32 runs at a quarter of the VALU rate) and the LDS reads (K
 // fragments through ds_read_b128 at ~237 B/clock per CU, V^T through
