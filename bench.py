@@ -104,6 +104,8 @@ def parse():
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-call figures of the other workloads (default line only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--measure", default="maxprob",
@@ -753,6 +755,50 @@ def per_call_times(wl, reps, use_graph):
 NEAR_BAND = {"maxprob": 1e-6, "margin": 1e-6, "neg_entropy": 5e-5, "logit_gap": 1e-5}
 
 
+# Workloads timed after the default line, per call, so that one default run
+# also covers the calls the other targets are set on: the Dream-7B-shaped
+# grouped-query attention (MFMA-bound) and its commit pass at three block
+# sizes, and the 32K-token prefix (KV-read-bound).
+OTHER_WORKLOADS = (("dream_gqa", 16), ("dream_gqa", 32), ("dream_gqa", 64), ("llada_p32k", None))
+
+
+def other_workloads(args, use_graph):
+    """Per-call attention and commit figures of OTHER_WORKLOADS (HIP graphs of
+    back-to-back launches over rotating input sets, as for the default line).
+    A workload that fails records its error instead of ending the run."""
+    import torch
+    res = {}
+    for name, bs in OTHER_WORKLOADS:
+        key = name if bs is None else f"{name}_b{bs}"
+        wl = None
+        try:
+            wl = Workload(name, bs, 1)
+            reps = max(args.call_reps, wl.n_sets)
+            wl.ensure_masks(reps + 1)
+            calls = per_call_times(wl, reps, use_graph)
+            sh = wl.sh
+            t_a = calls["d2f_block_attn"] * 1e-3
+            t_c = calls["d2f_confidence_commit"] * 1e-3
+            a_flops, a_bytes = attn_flops(sh), attn_bytes(sh)
+            c_bytes = commit_bytes(wl.n_masked, wl.rows, wl.cfg["vocab"])
+            tflops, gbs, cgbs = a_flops / t_a / 1e12, a_bytes / t_a / 1e9, c_bytes / t_c / 1e9
+            res[key] = {
+                "workload": wl.cfg["workload"],
+                "attn": {"avg_us": round(t_a * 1e6, 3), "tflops": round(tflops, 3),
+                         "frac_mfma": round(tflops / PEAK_BF16_TFLOPS, 4), "gbs": round(gbs, 2),
+                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "flops": a_flops,
+                         "bytes": a_bytes},
+                "commit": {"avg_us": round(t_c * 1e6, 3), "logit_gbs": round(cgbs, 2),
+                           "frac_hbm": round(cgbs / PEAK_HBM_GBS, 4), "bytes": c_bytes},
+                "per_call_graph_launches": reps, "input_sets": wl.n_sets}
+        except Exception as e:  # a failure here must not cost the default line
+            res[key] = {"error": f"{type(e).__name__}: {e}"[:300]}
+        finally:
+            del wl
+            torch.cuda.empty_cache()
+    return res
+
+
 def near_ties(wl):
     """Commit decisions too close to call, from the GPU's own fp32 confidences
     of the last commit call: MASKED rows within the measure's band of the
@@ -1277,6 +1323,11 @@ def main():
         rec["reuse"] = reuse_times(wl, call_reps, use_graph)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if args.config == "llada_batch16" and not (args.no_other_workloads or args.paged or
+                                               args.round_prefix or args.reuse):
+        del wl, warm, timed
+        torch.cuda.empty_cache()
+        rec["other_workloads"] = other_workloads(args, use_graph)
     print(json.dumps(rec), flush=True)
 
 

@@ -108,3 +108,26 @@ def test_stall_breakdown_shares_and_per_wave_counts():
     assert r["instructions_per_wave"]["mfma"] == 7.0 and r["instructions_per_wave"]["salu"] == 3.5
     assert r["mfma_busy_cycles_per_simd"] == 2 and r["coexec_share_of_mfma_busy"] == 0.25
     assert all(len(cs) <= 8 for cs in bench.STALL_COUNTERS)  # one pass holds <= 8 SQ counters
+
+
+def test_other_workloads_name_configs_the_targets_are_set_on():
+    import workloads as W
+    names = set()
+    for name, bs in bench.OTHER_WORKLOADS:
+        cfg = W.config(name, block_size=bs)
+        sh = cfg["shape"]
+        names.add((name, sh.block_size))
+        if name == "dream_gqa":  # grouped-query, MFMA-bound at these shapes
+            assert sh.n_heads_q > sh.n_heads_kv and sh.block_size == bs
+            assert bench.attn_flops(sh) / bench.attn_bytes(sh) > 200
+    assert {("dream_gqa", 16), ("dream_gqa", 32), ("dream_gqa", 64)} <= names
+    assert any(n == "llada_p32k" for n, _ in names)
+    import sys
+    old = sys.argv  # parse() reads sys.argv
+    try:
+        sys.argv = ["bench.py", "--no-other-workloads"]
+        assert bench.parse().no_other_workloads
+        sys.argv = ["bench.py"]
+        assert not bench.parse().no_other_workloads
+    finally:
+        sys.argv = old
