@@ -34,7 +34,8 @@
 //    and the first joins the two exactly.  Measured on MI355X (Dream-7B
 //    shape, block 32, 96-row units): 43.2-44.7 vs 47.0-48.1 us.  Each step
 //    of this mode reads the next tile's V^T fragments at its end, before
-//    the barrier.
+//    the barrier.  In units of at most 3 blocks, two of the waves left
+//    without a block issue all of the tile loads, and the others none.
 //  * Keys are processed in halves of 32, software-pipelined within a wave:
 //    while the matrix cores compute the scores of half h + 1, the vector
 //    units turn the scores of half h into probabilities; then half h's PV
@@ -157,8 +158,19 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   const int wb = KS ? (((wave & 3) + 2 * kg) & 3) : wave;  // its first block
   constexpr int BSTRIDE = KS ? 4 : kGqaWaves;
   const int nq = (wb < nblk) + (wb + BSTRIDE < nblk);  // this wave's blocks: 0, 1, 2
+  // Key-split units of at most 3 blocks leave waves 3 and 5 (at least)
+  // without a block.  Those two issue every direct load of a tile (loader
+  // 0 the even 1 KB blocks, loader 1 the odd ones) and the waves that
+  // compute issue none, so each step's chain of barrier, LDS reads, MFMAs
+  // and softmax carries no load issue (measured on MI355X, Dream-shaped
+  // block 16, 48-row units: 27.5-27.6 vs 30.9-31.0 us).  Paged caches keep
+  // the per-wave loads: a wave's page entries cover its own 8-row group.
+  const bool ldmode = KS && !PAGED && nblk <= 3;
+  const bool is_loader = ldmode && (wave == 3 || wave == 5);
+  const int li = wave == 3 ? 0 : 1;  // loader index
 
-  // Loader: wave w copies 1 KB blocks w, w + 8, ... of each of K and V; lane
+  // Loader: wave w copies 1 KB blocks w, w + 8, ... of each of K and V (in
+  // the loader mode above, loader i copies blocks i, i + 2, ...); lane
   // l of block j carries the 16 bytes that belong at LDS position (row
   // RPB j + l / CPR, chunk l % CPR), i.e. global chunk (l % CPR) ^ swz(row).
   // A tile's rows all come from the cache or all from the window, so the
@@ -232,11 +244,13 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       load_kv16<SHARED>((const char*)a.vc + pbase, off, sb + TILE + blk * 1024);
     }
   };
-  auto issue = [&](auto J, int t) __attribute__((always_inline)) {
+  auto issue = [&](auto J, int t, auto LMc) __attribute__((always_inline)) {
+    constexpr int LM = decltype(LMc)::value;
     if constexpr (PAGED) {
       issue_paged(J, t);
       return;
     }
+    if constexpr (LM == 2) return;
     const unsigned sb = (unsigned)(uintptr_t)stage_buf<decltype(J)::value, SB>();
     int lo, nv;
     tile_span(t, nct, P, k_end, lo, nv);
@@ -244,9 +258,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     const size_t o = (size_t)(in_cache ? lo : lo - P) * D;
     const char* kb = (const char*)((in_cache ? kc : kw) + o);
     const char* vb = (const char*)((in_cache ? vc : vw) + o);
+    constexpr int PER = LM == 1 ? NBLK / 2 : LPW;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wave + kGqaWaves * i;
+    for (int i = 0; i < PER; ++i) {
+      const int blk = LM == 1 ? li + 2 * i : wave + kGqaWaves * i;
       const int row = RPB * blk + lane / CPR;
       const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
       load_kv16<SHARED>(kb, off, sb + blk * 1024);
@@ -255,10 +270,13 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   };
   // Workgroup barrier between phases: this wave's LDS reads have returned
   // and at most `pending` tiles of its direct loads are still in flight (1:
-  // the tile requested last; 2: the last two).
-  auto barrier = [&](int pending) __attribute__((always_inline)) {
-    if (pending >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LOADS));
-    else if (pending == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LOADS));
+  // the tile requested last; 2: the last two).  LM: the wave's load mode
+  // (0: its share of every tile, 1: a loader's half of every tile, 2: none).
+  auto barrier = [&](int pending, auto LMc) __attribute__((always_inline)) {
+    constexpr int LM = decltype(LMc)::value;
+    constexpr int NL = PAGED ? LOADS : LM == 0 ? LOADS : LM == 1 ? NBLK : 0;
+    if (pending >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NL));
+    else if (pending == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NL));
     else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -270,9 +288,14 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   if constexpr (PAGED) {
     if (n > 0) pe_cur = entries(0);
   }
-  if (0 < n) issue(ic<0>{}, 0);
-  if (1 < n) issue(ic<1>{}, 1);
-  if (2 < n) issue(ic<2>{}, 2);
+  auto prologue = [&](auto LMc) __attribute__((always_inline)) {
+    if (0 < n) issue(ic<0>{}, 0, LMc);
+    if (1 < n) issue(ic<1>{}, 1, LMc);
+    if (2 < n) issue(ic<2>{}, 2, LMc);
+  };
+  if (!ldmode) prologue(ic<0>{});
+  else if (is_loader) prologue(ic<1>{});
+  else prologue(ic<2>{});
 
   // The wave's query rows: block qb is the unit's block wave + 8 qb; lane
   // (lc, lg) holds row lc of it (MFMA column lc).
@@ -299,7 +322,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // Retire the query loads and the first tiles here, so that no wait in the
   // loop has to count them; the barrier publishes tile 0 (and 1, 2).
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  if (n > 0) barrier(0);
+  if (n > 0) barrier(0, ic<0>{});
 
   f32x4 o[DBLK][2];
 #pragma unroll
@@ -485,8 +508,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       pv(QBc, va);
       prepare(QBc, 2 * t + 1, sb);
       // step 2t + 1: the next tile's first half.
-      barrier(t + 2 < n ? 1 : 0);
-      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
+      barrier(t + 2 < n ? 1 : 0, ic<0>{});
+      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3, ic<0>{});
       if (t + 1 < n) {
         bf16x8 ka[2][KSTEPS];
         kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2, ka);
@@ -513,7 +536,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // calls: block 16 31.1-31.3 vs 31.4-31.5 us, block 32 39.7-39.9 vs
   // 40.8-40.9 us).  Tile t - 1 is last read in step t - 2, so after barrier
   // t its stage receives tile t + 3.
-  auto run_ks = [&](auto QBc) __attribute__((always_inline)) {
+  auto run_ks = [&](auto QBc, auto LMc) __attribute__((always_inline)) {
     bf16x8 va[DBLK];
     {
       bf16x8 ka[2][KSTEPS];
@@ -526,8 +549,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       constexpr int JK = decltype(J)::value;
       f32x4 (&scur)[2][2] = (JK & 1) ? sb : sa;
       f32x4 (&snext)[2][2] = (JK & 1) ? sa : sb;
-      barrier(t + 2 < n ? 1 : 0);
-      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3);
+      barrier(t + 2 < n ? 1 : 0, LMc);
+      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3, LMc);
       if (t + 1 < n) {
         bf16x8 ka[2][KSTEPS];
         kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2 + kg, ka);
@@ -549,9 +572,15 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   };
   if (n > 0) {
     if constexpr (KS) {
-      if (nq == 2) run_ks(ic<2>{});
-      else if (nq == 1) run_ks(ic<1>{});
-      else run_ks(ic<0>{});
+      if (ldmode) {
+        if (is_loader) run_ks(ic<0>{}, ic<1>{});
+        else if (nq == 1) run_ks(ic<1>{}, ic<2>{});
+        else run_ks(ic<0>{}, ic<2>{});
+      } else {
+        if (nq == 2) run_ks(ic<2>{}, ic<0>{});
+        else if (nq == 1) run_ks(ic<1>{}, ic<0>{});
+        else run_ks(ic<0>{}, ic<0>{});
+      }
     } else {
       if (nq == 2) run(ic<2>{});
       else if (nq == 1) run(ic<1>{});
