@@ -158,16 +158,29 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   const int wb = KS ? (((wave & 3) + 2 * kg) & 3) : wave;  // its first block
   constexpr int BSTRIDE = KS ? 4 : kGqaWaves;
   const int nq = (wb < nblk) + (wb + BSTRIDE < nblk);  // this wave's blocks: 0, 1, 2
-  // Key-split units of at most 3 blocks leave waves 3 and 5 (at least)
-  // without a block.  Those two issue every direct load of a tile (loader
-  // 0 the even 1 KB blocks, loader 1 the odd ones) and the waves that
-  // compute issue none, so each step's chain of barrier, LDS reads, MFMAs
-  // and softmax carries no load issue (measured on MI355X, Dream-shaped
-  // block 16, 48-row units: 27.5-27.6 vs 30.9-31.0 us).  Paged caches keep
-  // the per-wave loads: a wave's page entries cover its own 8-row group.
-  const bool ldmode = KS && !PAGED && nblk <= 3;
-  const bool is_loader = ldmode && (wave == 3 || wave == 5);
-  const int li = wave == 3 ? 0 : 1;  // loader index
+  // Who issues a tile's direct loads (the load mode LM of this wave).  The
+  // waves that hold the most blocks set the pace of every step, so they
+  // issue none (LM 2) and lighter waves issue all of them:
+  //  * key-split units of at most 3 blocks leave waves 3 and 5 without a
+  //    block; those two take the even and the odd 1 KB blocks (LM 1);
+  //  * otherwise, on each SIMD the wave of the pair (s, s + 4) with fewer
+  //    blocks, the second one on a tie, takes blocks s, s + 4, ... (LM 3).
+  // Measured on MI355X, Dream-shaped calls, before -> after: block 16
+  // 30.8-31.0 -> 27.5-27.6 us, block 32 40.0-40.2 -> 37.9-38.0 us, block 64
+  // 59.0-59.3 -> 56.9-57.3 us.  Paged caches keep a share of every tile on
+  // every wave (LM 0): a wave's page entries cover its own 8-row group.
+  auto blocks_of = [&](int w) {
+    const int g = KS ? (w >> 2) : 0;
+    const int b = KS ? (((w & 3) + 2 * g) & 3) : w;
+    return (b < nblk) + (b + BSTRIDE < nblk);
+  };
+  const int simd = wave & 3;
+  const bool two_loaders = KS && nblk <= 3;
+  const int lmode =
+      PAGED ? 0
+      : two_loaders ? ((wave == 3 || wave == 5) ? 1 : 2)
+                    : (wave == (blocks_of(simd) < blocks_of(simd + 4) ? simd : simd + 4) ? 3 : 2);
+  const int li = wave == 3 ? 0 : 1;  // LM 1: loader index
 
   // Loader: wave w copies 1 KB blocks w, w + 8, ... of each of K and V (in
   // the loader mode above, loader i copies blocks i, i + 2, ...); lane
@@ -258,10 +271,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     const size_t o = (size_t)(in_cache ? lo : lo - P) * D;
     const char* kb = (const char*)((in_cache ? kc : kw) + o);
     const char* vb = (const char*)((in_cache ? vc : vw) + o);
-    constexpr int PER = LM == 1 ? NBLK / 2 : LPW;
+    constexpr int PER = LM == 1 ? NBLK / 2 : LM == 3 ? NBLK / 4 : LPW;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int blk = LM == 1 ? li + 2 * i : wave + kGqaWaves * i;
+      const int blk = LM == 1 ? li + 2 * i : LM == 3 ? simd + 4 * i : wave + kGqaWaves * i;
       const int row = RPB * blk + lane / CPR;
       const int off = min(row, nv - 1) * RS + 16 * ((lane % CPR) ^ swz<D>(row));
       load_kv16<SHARED>(kb, off, sb + blk * 1024);
@@ -270,11 +283,10 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   };
   // Workgroup barrier between phases: this wave's LDS reads have returned
   // and at most `pending` tiles of its direct loads are still in flight (1:
-  // the tile requested last; 2: the last two).  LM: the wave's load mode
-  // (0: its share of every tile, 1: a loader's half of every tile, 2: none).
+  // the tile requested last; 2: the last two), for a wave of load mode LM.
   auto barrier = [&](int pending, auto LMc) __attribute__((always_inline)) {
     constexpr int LM = decltype(LMc)::value;
-    constexpr int NL = PAGED ? LOADS : LM == 0 ? LOADS : LM == 1 ? NBLK : 0;
+    constexpr int NL = LM == 0 ? LOADS : LM == 1 ? NBLK : LM == 3 ? NBLK / 2 : 0;
     if (pending >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * NL));
     else if (pending == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(NL));
     else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
@@ -293,9 +305,17 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     if (1 < n) issue(ic<1>{}, 1, LMc);
     if (2 < n) issue(ic<2>{}, 2, LMc);
   };
-  if (!ldmode) prologue(ic<0>{});
-  else if (is_loader) prologue(ic<1>{});
-  else prologue(ic<2>{});
+  // Runs f with this wave's load mode as a compile-time constant.
+  auto with_lm = [&](auto&& f) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      f(ic<0>{});
+    } else {
+      if (lmode == 1) f(ic<1>{});
+      else if (lmode == 3) f(ic<3>{});
+      else f(ic<2>{});
+    }
+  };
+  with_lm(prologue);
 
   // The wave's query rows: block qb is the unit's block wave + 8 qb; lane
   // (lc, lg) holds row lc of it (MFMA column lc).
@@ -487,7 +507,7 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
   // Within a step the K fragments of the next half are requested before
   // the V^T fragments of this one: LDS returns reads in order, and the
   // scores' MFMAs, which come first, then wait only for the K reads.
-  auto run = [&](auto QBc) __attribute__((always_inline)) {
+  auto run = [&](auto QBc, auto LMc) __attribute__((always_inline)) {
     {
       bf16x8 ka[2][KSTEPS];
       kread(ic<0>{}, QBc, 0, ka);
@@ -508,8 +528,8 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
       pv(QBc, va);
       prepare(QBc, 2 * t + 1, sb);
       // step 2t + 1: the next tile's first half.
-      barrier(t + 2 < n ? 1 : 0, ic<0>{});
-      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3, ic<0>{});
+      barrier(t + 2 < n ? 1 : 0, LMc);
+      if (t + 3 < n) issue(ic<(JK + 3) % NST>{}, t + 3, LMc);
       if (t + 1 < n) {
         bf16x8 ka[2][KSTEPS];
         kread(ic<(JK + 1) % NST>{}, QBc, 2 * t + 2, ka);
@@ -571,21 +591,20 @@ __global__ __launch_bounds__(kGqaThreads, 1) void attn_gqa_kernel(const AttnArgs
     }
   };
   if (n > 0) {
-    if constexpr (KS) {
-      if (ldmode) {
-        if (is_loader) run_ks(ic<0>{}, ic<1>{});
-        else if (nq == 1) run_ks(ic<1>{}, ic<2>{});
-        else run_ks(ic<0>{}, ic<2>{});
+    with_lm([&](auto LMc) __attribute__((always_inline)) {
+      constexpr int LM = decltype(LMc)::value;
+      if constexpr (LM == 1) {
+        if constexpr (KS) run_ks(ic<0>{}, LMc);  // the two loaders hold no block
+      } else if constexpr (KS) {
+        if (nq == 2) run_ks(ic<2>{}, LMc);
+        else if (nq == 1) run_ks(ic<1>{}, LMc);
+        else run_ks(ic<0>{}, LMc);
       } else {
-        if (nq == 2) run_ks(ic<2>{}, ic<0>{});
-        else if (nq == 1) run_ks(ic<1>{}, ic<0>{});
-        else run_ks(ic<0>{}, ic<0>{});
+        if (nq == 2) run(ic<2>{}, LMc);
+        else if (nq == 1) run(ic<1>{}, LMc);
+        else run(ic<0>{}, LMc);
       }
-    } else {
-      if (nq == 2) run(ic<2>{});
-      else if (nq == 1) run(ic<1>{});
-      else run(ic<0>{});
-    }
+    });
   }
 
   // KS: waves 4-7 hand (m, l, O) of each block to the wave of keys 0-31
