@@ -98,14 +98,17 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llada_batch16", choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k", "llada_p128k"])
+    ap.add_argument("--config", default=None,
+                    choices=["llada_p512", "llada_batch16", "dream_gqa", "llada_p32k", "llada_p128k"],
+                    help="workload (default llada_batch16; only a run without --config adds "
+                         "the per-call figures of the other workloads)")
     ap.add_argument("--block-size", type=int, default=None, help="dream_gqa block size (16/32/64)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--call-reps", type=int, default=20, help="launches per per-call timing graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle CPU-baseline budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
-                    help="skip the per-call figures of the other workloads (default line only)")
+                    help="skip the per-call figures of the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--measure", default="maxprob",
@@ -145,7 +148,13 @@ def parse():
                     help="turn four rocprofv3 --pmc output dirs (FETCH_SIZE / WRITE_SIZE of "
                          "the copy calibration and of a bench run of --config) into "
                          "profiles/traffic_<config>.txt; needs no GPU")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # The default line (no --config) also times the other workloads per call;
+    # a run that names its workload, as the profiling commands do, does not.
+    args.other_workloads = args.config is None and not args.no_other_workloads
+    if args.config is None:
+        args.config = "llada_batch16"
+    return args
 
 
 COPY_BYTES = 512 << 20
@@ -1323,8 +1332,7 @@ def main():
         rec["reuse"] = reuse_times(wl, call_reps, use_graph)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    if args.config == "llada_batch16" and not (args.no_other_workloads or args.paged or
-                                               args.round_prefix or args.reuse):
+    if args.other_workloads and not (args.paged or args.round_prefix or args.reuse):
         del wl, warm, timed
         torch.cuda.empty_cache()
         rec["other_workloads"] = other_workloads(args, use_graph)

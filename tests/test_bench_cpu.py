@@ -125,9 +125,14 @@ def test_other_workloads_name_configs_the_targets_are_set_on():
     import sys
     old = sys.argv  # parse() reads sys.argv
     try:
+        sys.argv = ["bench.py", "--gpus", "1", "--steps", "20", "--warmup", "5"]
+        a = bench.parse()
+        assert a.other_workloads and a.config == "llada_batch16"
         sys.argv = ["bench.py", "--no-other-workloads"]
-        assert bench.parse().no_other_workloads
-        sys.argv = ["bench.py"]
-        assert not bench.parse().no_other_workloads
+        assert not bench.parse().other_workloads
+        # a run that names its workload (the profiling commands) times only that
+        sys.argv = ["bench.py", "--config", "llada_batch16", "--steps", "2"]
+        a = bench.parse()
+        assert not a.other_workloads and a.config == "llada_batch16"
     finally:
         sys.argv = old
